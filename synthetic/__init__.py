@@ -1,0 +1,208 @@
+"""Seeded synthetic inputs shared, as data only, by the tests, the bench and
+the oracle checks.  This module holds none of the attention arithmetic: it
+draws standard-normal samples, rounds them to bfloat16 (round to nearest,
+ties to even) when asked, and lays them out in the documented shapes.
+
+Recipe
+------
+Every (tensor, batch index) slice has its own stream,
+``numpy.random.default_rng([seed, tensor_id, b])``, drawn with
+``standard_normal(shape, float32)``; tensor ids are q=0, k=1, v=2 (prefill and
+MQA/GQA decode) and q_abs=0, latent=1 (MLA).  Varying decode lengths come
+first, from ``default_rng([seed, 99]).integers(lo, hi, endpoint=True)``.
+Per-slice streams let a check regenerate one sequence of a multi-gigabyte
+cache without drawing the rest.  Cache rows at or beyond ``seq_lens[b]`` are
+NaN, so any out-of-range read poisons the result.
+
+bfloat16 tensors are kept as ``uint16`` bit patterns (what the device reads);
+``Tensor.f32()`` gives their exact float32 values (what the oracle reads).
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+__all__ = [
+    "bf16_bits",
+    "bf16_to_f32",
+    "round_bf16",
+    "Tensor",
+    "prefill_inputs",
+    "decode_inputs",
+    "mla_inputs",
+    "draw_lengths",
+    "Workload",
+    "WORKLOADS",
+]
+
+_BF16_NAN = np.uint16(0x7FC0)
+
+
+def bf16_bits(x):
+    """float32 array -> uint16 bfloat16 bit patterns, round-to-nearest-even.
+    NaN maps to a quiet NaN pattern."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    r = ((u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)).astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        r[nan] = _BF16_NAN
+    return r
+
+
+def bf16_to_f32(bits):
+    """uint16 bfloat16 bit patterns -> exact float32 values."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def round_bf16(x):
+    return bf16_to_f32(bf16_bits(x))
+
+
+@dataclass
+class Tensor:
+    """One input: float32 values (``dtype == "f32"``) or bf16 bit patterns."""
+    data: np.ndarray              # float32 or uint16 (bf16 bits)
+    dtype: str = "f32"
+
+    @property
+    def shape(self):
+        return self.data.shape
+
+    def f32(self, index=...):
+        """Exact float32 values of ``data[index]``."""
+        part = self.data[index]
+        return bf16_to_f32(part) if self.dtype == "bf16" else np.asarray(part, dtype=np.float32)
+
+
+def _draw(seed, tid, b, shape):
+    return np.random.default_rng([seed, tid, b]).standard_normal(shape, dtype=np.float32)
+
+
+def _store(shape, dtype):
+    if dtype == "bf16":
+        return np.empty(shape, dtype=np.uint16)
+    if dtype == "f32":
+        return np.empty(shape, dtype=np.float32)
+    raise ValueError(dtype)
+
+
+def _put(dst, idx, vals, dtype):
+    dst[idx] = bf16_bits(vals) if dtype == "bf16" else vals
+
+
+def _nan(dtype):
+    return _BF16_NAN if dtype == "bf16" else np.float32(np.nan)
+
+
+def prefill_slice(seed, tid, b, H, T, D):
+    """float32 draw of one batch slice ``[H, T, D]`` of q (tid 0), k (1), v (2)."""
+    return _draw(seed, tid, b, (H, T, D))
+
+
+def prefill_inputs(B, Hq, Hkv, T, D, dtype="bf16", seed=0, d_v=None):
+    """q [B,Hq,T,D], k [B,Hkv,T,D], v [B,Hkv,T,d_v], iid N(0,1)."""
+    d_v = D if d_v is None else d_v
+    out = []
+    for tid, (H, dd) in enumerate(((Hq, D), (Hkv, D), (Hkv, d_v))):
+        t = _store((B, H, T, dd), dtype)
+        for b in range(B):
+            _put(t, b, _draw(seed, tid, b, (H, T, dd)), dtype)
+        out.append(Tensor(t, dtype))
+    return tuple(out)
+
+
+def draw_lengths(B, lengths, L_max, seed):
+    """seq_lens int32 [B]: None -> all L_max; int -> all equal; (lo, hi) ->
+    uniform integers in [lo, hi]; a sequence -> taken as given."""
+    if lengths is None:
+        return np.full(B, L_max, dtype=np.int32)
+    if isinstance(lengths, tuple):
+        lo, hi = lengths
+        return np.random.default_rng([seed, 99]).integers(lo, hi, endpoint=True, size=B).astype(np.int32)
+    if np.ndim(lengths) == 1:
+        return np.asarray(lengths, dtype=np.int32).copy()
+    return np.full(B, int(lengths), dtype=np.int32)
+
+
+def _cache(seed, tid, B, H, L_max, D, seq_lens, dtype, nan_pad, squeeze_head=False):
+    shape = (B, L_max, D) if squeeze_head else (B, H, L_max, D)
+    t = _store(shape, dtype)
+    for b in range(B):
+        L = int(seq_lens[b])
+        if squeeze_head:
+            _put(t, (b, slice(0, L)), _draw(seed, tid, b, (L, D)), dtype)
+            if L < L_max:
+                t[b, L:] = _nan(dtype) if nan_pad else 0
+        else:
+            _put(t, (b, slice(None), slice(0, L)), _draw(seed, tid, b, (H, L, D)), dtype)
+            if L < L_max:
+                t[b, :, L:] = _nan(dtype) if nan_pad else 0
+    return Tensor(t, dtype)
+
+
+def decode_inputs(B, Hq, Hkv, L_max, D, dtype="bf16", seed=0, lengths=None,
+                  nan_pad=True, d_v=None):
+    """q [B,Hq,D]; k cache [B,Hkv,L_max,D]; v cache [B,Hkv,L_max,d_v];
+    seq_lens int32 [B].  Rows >= seq_lens[b] are NaN when ``nan_pad``."""
+    d_v = D if d_v is None else d_v
+    seq_lens = draw_lengths(B, lengths, L_max, seed)
+    q = _store((B, Hq, D), dtype)
+    for b in range(B):
+        _put(q, b, _draw(seed, 0, b, (Hq, D)), dtype)
+    k = _cache(seed, 1, B, Hkv, L_max, D, seq_lens, dtype, nan_pad)
+    v = _cache(seed, 2, B, Hkv, L_max, d_v, seq_lens, dtype, nan_pad)
+    return Tensor(q, dtype), k, v, seq_lens
+
+
+def decode_slice(seed, b, Hq, Hkv, L, D, d_v=None):
+    """float32 draws of sequence b only: (q [Hq,D], k [Hkv,L,D], v [Hkv,L,d_v])."""
+    d_v = D if d_v is None else d_v
+    return (_draw(seed, 0, b, (Hq, D)), _draw(seed, 1, b, (Hkv, L, D)),
+            _draw(seed, 2, b, (Hkv, L, d_v)))
+
+
+def mla_inputs(B, H, L_max, d_kv=576, dtype="bf16", seed=0, lengths=None,
+               nan_pad=True):
+    """q_abs [B,H,d_kv]; latent cache [B,L_max,d_kv]; seq_lens int32 [B]."""
+    seq_lens = draw_lengths(B, lengths, L_max, seed)
+    q = _store((B, H, d_kv), dtype)
+    for b in range(B):
+        _put(q, b, _draw(seed, 0, b, (H, d_kv)), dtype)
+    kv = _cache(seed, 1, B, 1, L_max, d_kv, seq_lens, dtype, nan_pad, squeeze_head=True)
+    return Tensor(q, dtype), kv, seq_lens
+
+
+def mla_slice(seed, b, H, L, d_kv=576):
+    """float32 draws of sequence b only: (q_abs [H,d_kv], latent [L,d_kv])."""
+    return _draw(seed, 0, b, (H, d_kv)), _draw(seed, 1, b, (L, d_kv))
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str                      # "prefill" | "decode" | "mla"
+    dtype: str
+    shape: dict = field(default_factory=dict)
+
+
+# The measured and parity-checked shapes (all iid N(0,1), seed 0).
+WORKLOADS = {
+    w.name: w for w in (
+        Workload("mqa_prefill_f32_b1_t128", "prefill", "f32",
+                 dict(B=1, Hq=16, Hkv=1, T=128, D=512)),
+        Workload("mqa_prefill_bf16_b2_t4096", "prefill", "bf16",
+                 dict(B=2, Hq=16, Hkv=1, T=4096, D=512)),
+        Workload("mqa_decode_bf16_b64_l8192", "decode", "bf16",
+                 dict(B=64, Hq=16, Hkv=1, L=8192, D=512, lengths=None)),
+        Workload("gqa_prefill_bf16_b1_t8192", "prefill", "bf16",
+                 dict(B=1, Hq=64, Hkv=8, T=8192, D=128)),
+        Workload("gqa_decode_bf16_b128_l1024to16384", "decode", "bf16",
+                 dict(B=128, Hq=64, Hkv=8, L=16384, D=128, lengths=(1024, 16384))),
+        Workload("mla_decode_bf16_b32_l32768", "mla", "bf16",
+                 dict(B=32, H=128, L=32768, D=576)),
+    )
+}
