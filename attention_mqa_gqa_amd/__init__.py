@@ -1,0 +1,237 @@
+"""Python binding of libmqa_attn.so (MQA / GQA / MLA-absorbed attention on
+MI355X).  Argument marshalling only: every step of the computation runs in
+the library's HIP kernels.  PyTorch provides device memory and the stream.
+
+The entry points carry the C ABI's names (see ``include/mqa_attn.h``):
+
+* :func:`mqa_prefill`          -- causal or full attention over a sequence;
+* :func:`mqa_decode`           -- one query token per sequence vs a KV cache;
+* :func:`mla_decode_absorbed`  -- absorbed MLA decode over a latent cache.
+
+The library must be built (``python attention_mqa_gqa_amd/build.py``); if it
+is missing or cannot be loaded, importing the bindings raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "LIB_PATH",
+    "MqaError",
+    "lib",
+    "mqa_prefill",
+    "mqa_prefill_workspace_size",
+    "mqa_decode",
+    "mqa_decode_workspace_size",
+    "mla_decode_absorbed",
+    "mla_decode_workspace_size",
+    "DTYPE_F32",
+    "DTYPE_BF16",
+    "EXPORTED_SYMBOLS",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmqa_attn.so")
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+
+EXPORTED_SYMBOLS = (
+    "mqa_attn_abi_version",
+    "mqa_status_string",
+    "mqa_last_hip_error_name",
+    "mqa_prefill_workspace_size",
+    "mqa_prefill",
+    "mqa_decode_workspace_size",
+    "mqa_decode",
+    "mla_decode_workspace_size",
+    "mla_decode_absorbed",
+)
+
+
+class MqaError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        detail = ""
+        if status == -4:
+            detail = f", {lib.mqa_last_hip_error_name().decode()}"
+        super().__init__(f"{what}: status {status} ({_status_string(status)}{detail})")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python attention_mqa_gqa_amd/build.py`")
+    l = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    l.mqa_attn_abi_version.restype = i
+    l.mqa_attn_abi_version.argtypes = []
+    l.mqa_status_string.restype = ctypes.c_char_p
+    l.mqa_status_string.argtypes = [i]
+    l.mqa_last_hip_error_name.restype = ctypes.c_char_p
+    l.mqa_last_hip_error_name.argtypes = []
+    l.mqa_prefill_workspace_size.restype = sz
+    l.mqa_prefill_workspace_size.argtypes = [i, i, i, i, i, i]
+    l.mqa_prefill.restype = i
+    l.mqa_prefill.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, sz, vp]
+    l.mqa_decode_workspace_size.restype = sz
+    l.mqa_decode_workspace_size.argtypes = [i, i, i, i, i]
+    l.mqa_decode.restype = i
+    l.mqa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
+    l.mla_decode_workspace_size.restype = sz
+    l.mla_decode_workspace_size.argtypes = [i, i, i]
+    l.mla_decode_absorbed.restype = i
+    l.mla_decode_absorbed.argtypes = [vp, vp, vp, vp, vp, i, i, i, f, i, i, vp, sz, vp]
+    return l
+
+
+lib = _load()
+
+
+def _status_string(status):
+    return lib.mqa_status_string(int(status)).decode()
+
+
+def _check(status, what):
+    if status != 0:
+        raise MqaError(status, what)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(dt):
+    torch = _torch()
+    if dt == torch.float32:
+        return DTYPE_F32
+    if dt == torch.bfloat16:
+        return DTYPE_BF16
+    raise TypeError(f"unsupported dtype {dt}; use torch.float32 or torch.bfloat16")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_ptr(stream, device):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _require(t, name, ndim):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def mqa_prefill_workspace_size(B, Hq, Hkv, T, head_dim, in_dtype):
+    return int(lib.mqa_prefill_workspace_size(B, Hq, Hkv, T, head_dim, in_dtype))
+
+
+def mqa_decode_workspace_size(B, Hq, Hkv, max_len, head_dim):
+    return int(lib.mqa_decode_workspace_size(B, Hq, Hkv, max_len, head_dim))
+
+
+def mla_decode_workspace_size(B, H, max_len):
+    return int(lib.mla_decode_workspace_size(B, H, max_len))
+
+
+def _workspace(nbytes, device, workspace):
+    torch = _torch()
+    if nbytes == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def mqa_prefill(q, k, v, causal=True, scale=None, out=None, out_dtype=None, lse=None,
+                workspace=None, stream=None):
+    """q [B,Hq,T,D], k/v [B,Hkv,T,D] -> out [B,Hq,T,D] (and lse [B,Hq,T] if given)."""
+    torch = _torch()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, nm, 4)
+    B, Hq, T, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, T, D) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, Hkv, T, D] matching q")
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise TypeError("q, k, v must share a dtype")
+    in_code = _dtype_code(q.dtype)
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, Hq, T, D), dtype=out_dtype, device=q.device)
+    _require(out, "out", 4)
+    if lse is not None:
+        _require(lse, "lse", 3)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    nbytes = mqa_prefill_workspace_size(B, Hq, Hkv, T, D, in_code)
+    ws, wsb = _workspace(nbytes, q.device, workspace)
+    st = lib.mqa_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, T, D, scale,
+                         1 if causal else 0, in_code, _dtype_code(out.dtype), _ptr(ws), wsb,
+                         _stream_ptr(stream, q.device))
+    _check(st, "mqa_prefill")
+    return out
+
+
+def mqa_decode(q, k_cache, v_cache, seq_lens, scale=None, out=None, out_dtype=None, lse=None,
+               workspace=None, stream=None):
+    """q [B,Hq,D], caches [B,Hkv,L_max,D], seq_lens int32 [B] -> out [B,Hq,D]."""
+    torch = _torch()
+    _require(q, "q", 3)
+    _require(k_cache, "k_cache", 4)
+    _require(v_cache, "v_cache", 4)
+    _require(seq_lens, "seq_lens", 1)
+    if seq_lens.dtype != torch.int32:
+        raise TypeError("seq_lens must be int32")
+    B, Hq, D = q.shape
+    Hkv, L_max = k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape != (B, Hkv, L_max, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [B, Hkv, L_max, D] matching q")
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype, device=q.device)
+    _require(out, "out", 3)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    nbytes = mqa_decode_workspace_size(B, Hq, Hkv, L_max, D)
+    ws, wsb = _workspace(nbytes, q.device, workspace)
+    st = lib.mqa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(out), _ptr(lse),
+                        B, Hq, Hkv, L_max, D, scale, _dtype_code(q.dtype), _dtype_code(out.dtype),
+                        _ptr(ws), wsb, _stream_ptr(stream, q.device))
+    _check(st, "mqa_decode")
+    return out
+
+
+def mla_decode_absorbed(q_abs, kv_cache, seq_lens, scale=None, out=None, out_dtype=None, lse=None,
+                        workspace=None, stream=None):
+    """q_abs [B,H,576], kv_cache [B,L_max,576], seq_lens int32 [B] -> out [B,H,512]."""
+    torch = _torch()
+    _require(q_abs, "q_abs", 3)
+    _require(kv_cache, "kv_cache", 3)
+    _require(seq_lens, "seq_lens", 1)
+    if seq_lens.dtype != torch.int32:
+        raise TypeError("seq_lens must be int32")
+    B, H, DK = q_abs.shape
+    if DK != 576 or kv_cache.shape[0] != B or kv_cache.shape[2] != 576:
+        raise ValueError("q_abs must be [B,H,576] and kv_cache [B,L_max,576]")
+    L_max = kv_cache.shape[1]
+    out_dtype = q_abs.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, H, 512), dtype=out_dtype, device=q_abs.device)
+    _require(out, "out", 3)
+    scale = 1.0 / math.sqrt(192.0) if scale is None else float(scale)
+    nbytes = mla_decode_workspace_size(B, H, L_max)
+    ws, wsb = _workspace(nbytes, q_abs.device, workspace)
+    st = lib.mla_decode_absorbed(_ptr(q_abs), _ptr(kv_cache), _ptr(seq_lens), _ptr(out), _ptr(lse),
+                                 B, H, L_max, scale, _dtype_code(q_abs.dtype), _dtype_code(out.dtype),
+                                 _ptr(ws), wsb, _stream_ptr(stream, q_abs.device))
+    _check(st, "mla_decode_absorbed")
+    return out

@@ -1,0 +1,178 @@
+// C ABI of libmqa_attn.so (declared in include/mqa_attn.h).
+// Every argument is validated here, on the host, before any HIP call; the
+// launchers in the kernel files receive only requests they support.
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/mqa_attn.h"
+#include "kernels.hpp"
+
+namespace {
+
+using mqa::DecodePlan;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool valid_dtype(int d) { return d == MQA_DTYPE_F32 || d == MQA_DTYPE_BF16; }
+
+size_t elem_bytes(int d) { return d == MQA_DTYPE_BF16 ? 2 : 4; }
+
+thread_local hipError_t g_last_hip_error = hipSuccess;
+
+// HIP keeps the last error of ANY runtime call made on this thread (by any
+// library) until someone reads it.  Read and drop such a stale error before
+// launching, so that the check after the launch reports only our launches.
+void clear_stale_error() { (void)hipGetLastError(); }
+
+int hip_status(hipError_t e) {
+    g_last_hip_error = e;
+    return e == hipSuccess ? MQA_OK : MQA_ERR_HIP;
+}
+
+// bf16 prefill: rows per workgroup must hold at least one full head group.
+bool prefill_bf16_supported(int head_dim, int G) {
+    if (head_dim != 128 && head_dim != 512) return false;
+    const mqa::PrefillPlan p = mqa::prefill_plan(head_dim, 1);
+    return G >= 1 && G <= p.rows_per_wg;
+}
+
+size_t decode_ws_bytes(int B, int Hq, int D, const DecodePlan& p) {
+    return (size_t)B * Hq * p.n_split * ((size_t)D + 2) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+int mqa_attn_abi_version(void) { return MQA_ATTN_ABI_VERSION; }
+
+const char* mqa_last_hip_error_name(void) { return hipGetErrorName(g_last_hip_error); }
+
+const char* mqa_status_string(int status) {
+    switch (status) {
+        case MQA_OK: return "ok";
+        case MQA_ERR_INVALID_ARG: return "invalid argument";
+        case MQA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+        case MQA_ERR_WORKSPACE: return "workspace missing or too small";
+        case MQA_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+size_t mqa_prefill_workspace_size(int B, int Hq, int Hkv, int T, int head_dim, int in_dtype) {
+    (void)Hq;
+    if (in_dtype != MQA_DTYPE_BF16 || B <= 0 || Hkv <= 0 || T <= 0 || head_dim <= 0) return 0;
+    const mqa::PrefillPlan p = mqa::prefill_plan(head_dim, 1);
+    if (p.kt <= 0) return 0;
+    const size_t tiles = ((size_t)T + p.kt - 1) / p.kt;
+    return (size_t)B * Hkv * tiles * p.kt * head_dim * 2;
+}
+
+int mqa_prefill(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv, int T,
+                int head_dim, float scale, int causal, int in_dtype, int out_dtype, void* workspace,
+                size_t workspace_bytes, void* stream) {
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || T < 0 || head_dim <= 0) return MQA_ERR_INVALID_ARG;
+    if (Hq % Hkv != 0) return MQA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return MQA_ERR_INVALID_ARG;
+    if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return MQA_ERR_INVALID_ARG;
+    if (B == 0 || T == 0) return MQA_OK;
+    if (!q || !k || !v || !out) return MQA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || (lse && ((uintptr_t)lse & 3u)))
+        return MQA_ERR_INVALID_ARG;
+    const int G = Hq / Hkv;
+    const bool bf = in_dtype == MQA_DTYPE_BF16;
+    if (bf) {
+        if (!prefill_bf16_supported(head_dim, G)) return MQA_ERR_UNSUPPORTED;
+    } else {
+        if (out_dtype != MQA_DTYPE_F32) return MQA_ERR_UNSUPPORTED;
+        if (head_dim % 64 != 0 || head_dim > 512) return MQA_ERR_UNSUPPORTED;
+    }
+    // the kernels address one (batch, KV head) slice of K with 32-bit byte offsets
+    if (bf && (size_t)T * head_dim * 2 > 0xFFFFFFFFull) return MQA_ERR_UNSUPPORTED;
+    const size_t need = mqa_prefill_workspace_size(B, Hq, Hkv, T, head_dim, in_dtype);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return MQA_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return MQA_ERR_INVALID_ARG;
+    }
+    mqa::PrefillArgs a;
+    a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.T = T; a.D = head_dim; a.G = G;
+    a.scale = scale; a.causal = causal != 0; a.in_bf16 = bf; a.out_f32 = out_dtype == MQA_DTYPE_F32;
+    a.workspace = workspace; a.stream = (hipStream_t)stream;
+    clear_stale_error();
+    return hip_status(mqa::prefill_launch(a));
+}
+
+size_t mqa_decode_workspace_size(int B, int Hq, int Hkv, int max_len, int head_dim) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || max_len <= 0 || head_dim <= 0) return 0;
+    return decode_ws_bytes(B, Hq, head_dim, mqa::decode_plan(B, Hkv, max_len, head_dim));
+}
+
+int mqa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens, void* out,
+               float* lse, int B, int Hq, int Hkv, int max_len, int head_dim, float scale, int dtype, int out_dtype,
+               void* workspace, size_t workspace_bytes, void* stream) {
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || max_len < 0 || head_dim <= 0) return MQA_ERR_INVALID_ARG;
+    if (Hq % Hkv != 0) return MQA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return MQA_ERR_INVALID_ARG;
+    if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return MQA_ERR_INVALID_ARG;
+    if (B == 0) return MQA_OK;
+    if (!q || !k_cache || !v_cache || !seq_lens || !out) return MQA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+        ((uintptr_t)seq_lens & 3u) || (lse && ((uintptr_t)lse & 3u)))
+        return MQA_ERR_INVALID_ARG;
+    const int G = Hq / Hkv;
+    if (dtype != MQA_DTYPE_BF16) return MQA_ERR_UNSUPPORTED;
+    if (head_dim != 128 && head_dim != 512) return MQA_ERR_UNSUPPORTED;
+    if (G > 16) return MQA_ERR_UNSUPPORTED;
+    if (max_len == 0) return MQA_ERR_INVALID_ARG;  // a cache with no rows cannot hold the current token
+    const DecodePlan plan = mqa::decode_plan(B, Hkv, max_len, head_dim);
+    const size_t need = decode_ws_bytes(B, Hq, head_dim, plan);
+    if (!workspace || workspace_bytes < need) return MQA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MQA_ERR_INVALID_ARG;
+    mqa::DecodeArgs a;
+    a.q = q; a.k = k_cache; a.v = v_cache; a.seq_lens = seq_lens; a.out = out; a.lse = lse;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.max_len = max_len; a.D = head_dim; a.G = G;
+    a.scale = scale; a.out_f32 = out_dtype == MQA_DTYPE_F32;
+    a.part_o = (float*)workspace;
+    a.part_ml = (float*)workspace + (size_t)B * Hq * plan.n_split * head_dim;
+    a.plan = plan; a.stream = (hipStream_t)stream;
+    clear_stale_error();
+    return hip_status(mqa::decode_launch(a));
+}
+
+size_t mla_decode_workspace_size(int B, int H, int max_len) {
+    if (B <= 0 || H <= 0 || max_len <= 0) return 0;
+    return decode_ws_bytes(B, H, 512, mqa::mla_plan(B, max_len));
+}
+
+int mla_decode_absorbed(const void* q_abs, const void* kv_cache, const int32_t* seq_lens, void* out, float* lse,
+                        int B, int H, int max_len, float scale, int dtype, int out_dtype, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+    if (B < 0 || H <= 0 || max_len < 0) return MQA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return MQA_ERR_INVALID_ARG;
+    if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return MQA_ERR_INVALID_ARG;
+    if (B == 0) return MQA_OK;
+    if (!q_abs || !kv_cache || !seq_lens || !out) return MQA_ERR_INVALID_ARG;
+    if (!aligned16(q_abs) || !aligned16(kv_cache) || !aligned16(out) || ((uintptr_t)seq_lens & 3u) ||
+        (lse && ((uintptr_t)lse & 3u)))
+        return MQA_ERR_INVALID_ARG;
+    if (dtype != MQA_DTYPE_BF16) return MQA_ERR_UNSUPPORTED;
+    if (H % 16 != 0 || H > 128) return MQA_ERR_UNSUPPORTED;
+    if (max_len == 0) return MQA_ERR_INVALID_ARG;
+    // one sequence's latent cache is addressed with 32-bit byte offsets
+    if ((size_t)max_len * 576 * 2 > 0xFFFFFFFFull) return MQA_ERR_UNSUPPORTED;
+    const DecodePlan plan = mqa::mla_plan(B, max_len);
+    const size_t need = decode_ws_bytes(B, H, 512, plan);
+    if (!workspace || workspace_bytes < need) return MQA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MQA_ERR_INVALID_ARG;
+    mqa::MlaArgs a;
+    a.q = q_abs; a.kv = kv_cache; a.seq_lens = seq_lens; a.out = out; a.lse = lse;
+    a.B = B; a.H = H; a.max_len = max_len; a.scale = scale; a.out_f32 = out_dtype == MQA_DTYPE_F32;
+    a.part_o = (float*)workspace;
+    a.part_ml = (float*)workspace + (size_t)B * H * plan.n_split * 512;
+    a.plan = plan; a.stream = (hipStream_t)stream;
+    clear_stale_error();
+    return hip_status(mqa::mla_launch(a));
+}
+
+}  // extern "C"

@@ -1,0 +1,113 @@
+// Device helpers shared by the gfx950 attention kernels: vector types, MFMA
+// wrappers, bf16 packing, wave reductions and the direct global->LDS copy.
+//
+// MFMA lane layouts used throughout (wave64, 16x16 output tiles):
+//   C/D  (f32x4): lane l holds C[4*(l/16) + i][l % 16], i = 0..3.
+//   A/B of v_mfma_f32_16x16x32_bf16 (8 bf16 per lane): lane l holds
+//        A[l % 16][k] / B[k][l % 16] for the 8 k of lane group g = l/16.
+//   A/B of v_mfma_f32_16x16x16_bf16 (4 bf16 per lane): the 4 k of group g.
+// The kernels only rely on A and B sharing one (group, slot) -> k map, so a
+// contraction pairs A slot j of group g with B slot j of group g.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mqa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Lazy rescaling: the running row maximum used for exponentiation is only
+// raised when a new score exceeds it by more than this many log2 units, so
+// probabilities stay below 2^kRescaleSlack and the accumulator rescale is
+// rare.  Exact: numerator and denominator share the same reference maximum.
+constexpr float kRescaleSlack = 8.0f;
+
+__device__ __forceinline__ f32x4 mfma_16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_16x16x16(const u32x2& a, const u32x2& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_16x16x4_f32(float a, float b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Round-to-nearest-even fp32 -> bf16 (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16 a = (bf16)lo, b = (bf16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ bf16x8 pack_bf16x8(const f32x4& lo, const f32x4& hi) {
+    u32x4 u;
+    u.x = pack_bf16x2(lo.x, lo.y);
+    u.y = pack_bf16x2(lo.z, lo.w);
+    u.z = pack_bf16x2(hi.x, hi.y);
+    u.w = pack_bf16x2(hi.z, hi.w);
+    return __builtin_bit_cast(bf16x8, u);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+// Byte permute: bytes 0-3 come from `lo`, 4-7 from `hi`.
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+constexpr uint32_t kSelLoHalves = 0x05040100u;  // {lo.h0, hi.h0}
+constexpr uint32_t kSelHiHalves = 0x07060302u;  // {lo.h1, hi.h1}
+
+// Max / sum over the four lanes l, l^16, l^32, l^48 (the four lane groups
+// that share one MFMA output column).
+__device__ __forceinline__ float max_over_groups(float v) {
+    v = fmaxf(v, __shfl_xor(v, 16));
+    v = fmaxf(v, __shfl_xor(v, 32));
+    return v;
+}
+__device__ __forceinline__ float sum_over_groups(float v) {
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+
+__device__ __forceinline__ u32x4 ldg16(const void* p) { return *(const u32x4*)p; }
+__device__ __forceinline__ bf16x8 ldg_bf16x8(const void* p) { return *(const bf16x8*)p; }
+
+// Asynchronous 16-byte copy global -> LDS.  Every lane supplies its own
+// global address; lane i's 16 bytes land at lds_base + 16*i (lds_base must be
+// the same for all lanes of the wave).  Completion is tracked by vmcnt.
+__device__ __forceinline__ void copy16_to_lds(const void* gptr, void* lds_base_wave) {
+    __builtin_amdgcn_global_load_lds(gptr, (lds_void*)lds_base_wave, 16, 0, 0);
+}
+
+// Same, with the source given as a wave-uniform base plus a 32-bit per-lane
+// byte offset (lets the compiler use an SGPR base and one VGPR offset).
+__device__ __forceinline__ void copy16_to_lds_off(const void* base, uint32_t byte_off, void* lds_base_wave) {
+    __builtin_amdgcn_global_load_lds((const char*)base + byte_off, (lds_void*)lds_base_wave, 16, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+}  // namespace mqa

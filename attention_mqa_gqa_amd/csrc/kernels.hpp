@@ -1,0 +1,83 @@
+// Internal interface between the C ABI (api.hip) and the kernel files.
+// Arguments reaching these launchers have been validated by the ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mqa {
+
+struct PrefillArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    float* lse;
+    int B, Hq, Hkv, T, D, G;
+    float scale;
+    bool causal;
+    bool in_bf16;
+    bool out_f32;
+    void* workspace;
+    hipStream_t stream;
+};
+
+struct PrefillPlan {
+    int rows_per_wg;  // query rows (heads x tokens) per workgroup, bf16 path
+    int kt;           // keys per K/V tile, bf16 path
+};
+
+PrefillPlan prefill_plan(int head_dim, int in_bf16);
+hipError_t prefill_launch(const PrefillArgs& a);
+
+// Split-KV decode plan shared by the workspace query and the launch.
+struct DecodePlan {
+    int chunk;    // cache rows per workgroup (per split)
+    int n_split;  // splits per sequence
+};
+
+DecodePlan decode_plan(int B, int Hkv, int max_len, int head_dim);
+DecodePlan mla_plan(int B, int max_len);
+
+struct DecodeArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const int32_t* seq_lens;
+    void* out;
+    float* lse;
+    int B, Hq, Hkv, max_len, D, G;
+    float scale;
+    bool out_f32;
+    float* part_o;   // [B*Hq*n_split, D]
+    float* part_ml;  // [B*Hq*n_split, 2]
+    DecodePlan plan;
+    hipStream_t stream;
+};
+
+hipError_t decode_launch(const DecodeArgs& a);
+
+struct MlaArgs {
+    const void* q;
+    const void* kv;
+    const int32_t* seq_lens;
+    void* out;
+    float* lse;
+    int B, H, max_len;
+    float scale;
+    bool out_f32;
+    float* part_o;   // [B*H*n_split, 512]
+    float* part_ml;  // [B*H*n_split, 2]
+    DecodePlan plan;
+    hipStream_t stream;
+};
+
+hipError_t mla_launch(const MlaArgs& a);
+
+// LSE merge of split partials (shared by both decode paths).
+hipError_t merge_launch(const float* part_o, const float* part_ml, const int32_t* seq_lens, void* out,
+                        float* lse, int B, int H, int max_len, int D, int chunk, int n_split, bool out_f32,
+                        hipStream_t stream);
+
+}  // namespace mqa

@@ -1,0 +1,152 @@
+/*
+ * mqa_attn.h -- C ABI of the MI355X (gfx950) attention library for query
+ * heads that share few key/value heads: MQA, GQA and the absorbed form of
+ * MLA.  Library: libmqa_attn.so (built from attention_mqa_gqa_amd/csrc).
+ *
+ * What is computed (source pages, by title and section):
+ *   out = softmax(scale * Q K^T  [+ causal mask]) V, per query head, where a
+ *   query head h reads key/value head h / (Hq / Hkv)
+ *     - single-head definition: "带你了解Attention,从MHA到DeepSeek"
+ *       (api.makesence.top) §1.2; causal mask and prefill/decode phases:
+ *       "GQA和MLA详解" (lzwjava.github.io) §1;
+ *     - head sharing (repeat_interleave on the head axis, done here by
+ *       indexing, never by copying): lzwjava §2, makesence §3.1-3.2,
+ *       "Full 路线：保留 softmax，压缩 K/V 表示" (walkerchi.com) §三;
+ *     - MQA with head_dim 512 and 16 query heads over one KV head: zdabc.icu
+ *       article on DeepSeek V4.1's MQA operator, sections
+ *       "head_dim = 512 为什么值得注意" and the MQA benchmark baseline;
+ *     - MLA decode on the cached latent after folding W_UK into the query and
+ *       W_UV into the output (matrix absorption) with a decoupled 64-d RoPE
+ *       key: lzwjava §3, makesence §4.3 and §4.5, walkerchi §四 4.2-4.3.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers, owned by the caller, row-major
+ *     with the last dimension contiguous, and 16-byte aligned.  The library
+ *     allocates nothing, keeps no state between calls, never synchronises,
+ *     and enqueues its kernels on `stream` (a hipStream_t; NULL = the default
+ *     stream).  Inputs are read-only; outputs and workspace are overwritten.
+ *   - Element types: MQA_DTYPE_F32 (IEEE float) or MQA_DTYPE_BF16 (bfloat16).
+ *     Products accumulate in fp32.  Probabilities are rounded to bf16 before
+ *     the P.V product when the inputs are bf16; fp32 inputs stay fp32 end to
+ *     end.  Conversions to bf16 round to nearest even.
+ *   - `lse` (optional, may be NULL) receives the natural-log log-sum-exp of
+ *     the scaled, masked scores of each query row, in fp32.
+ *   - Every argument is validated on the host before any HIP call; a rejected
+ *     call returns a negative status and enqueues nothing.  A zero batch or
+ *     zero sequence length is a valid empty call (returns MQA_OK, enqueues
+ *     nothing).  The library never aborts; kernel-launch failures are
+ *     reported as MQA_ERR_HIP.
+ *   - Calls on different streams may overlap only if their outputs and
+ *     workspaces do not alias.
+ */
+#ifndef MQA_ATTN_H
+#define MQA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MQA_ATTN_ABI_VERSION 1
+
+typedef enum {
+    MQA_DTYPE_F32 = 0,
+    MQA_DTYPE_BF16 = 1
+} mqa_dtype;
+
+typedef enum {
+    MQA_OK = 0,
+    MQA_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, bad size or scale   */
+    MQA_ERR_UNSUPPORTED = -2,  /* valid request outside what the kernels cover */
+    MQA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required   */
+    MQA_ERR_HIP = -4           /* the HIP runtime reported a launch error      */
+} mqa_status;
+
+/* Version of this ABI (MQA_ATTN_ABI_VERSION of the built library). */
+int mqa_attn_abi_version(void);
+
+/* Static description of a status code; never NULL. */
+const char* mqa_status_string(int status);
+
+/* Name of the HIP error behind the most recent MQA_ERR_HIP (or "hipSuccess")
+ * returned on the calling thread; never NULL.  Each entry point discards any
+ * error left pending by earlier, unrelated HIP calls on the thread before it
+ * launches, so MQA_ERR_HIP always refers to this library's own launches. */
+const char* mqa_last_hip_error_name(void);
+
+/* ---------------------------------------------------------------- prefill
+ * Causal (or full) attention over a whole sequence.
+ *   q   [B, Hq,  T, D]      k, v [B, Hkv, T, D]      out [B, Hq, T, D]
+ *   lse [B, Hq, T] fp32 or NULL
+ *   causal != 0: key j is visible to query i iff j <= i (square, top-left
+ *   aligned: query i is the token at position i).
+ *   scale: the factor on Q.K^T, normally 1/sqrt(D).  Must be finite.
+ * Supported: Hq % Hkv == 0;
+ *   in_dtype BF16 -> out_dtype BF16 or F32, D in {128, 512}, and the group
+ *     size G = Hq/Hkv a power of two with G <= 128 (D=512) or G <= 256
+ *     (D=128);
+ *   in_dtype F32 -> out_dtype F32, D a multiple of 64 up to 512, any G.
+ * Workspace: bf16 inputs need `mqa_prefill_workspace_size()` bytes (a tiled,
+ * transposed copy of V that the library writes first); F32 needs none
+ * (workspace may be NULL with workspace_bytes 0).
+ */
+size_t mqa_prefill_workspace_size(int B, int Hq, int Hkv, int T, int head_dim,
+                                  int in_dtype);
+
+int mqa_prefill(const void* q, const void* k, const void* v, void* out, float* lse,
+                int B, int Hq, int Hkv, int T, int head_dim, float scale, int causal,
+                int in_dtype, int out_dtype,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* ----------------------------------------------------------------- decode
+ * One new query token per sequence against a KV cache (split-KV: the valid
+ * cache of each sequence is cut into chunks processed in parallel, then the
+ * chunk results are merged by log-sum-exp in a fixed order, so the result is
+ * deterministic run to run).
+ *   q [B, Hq, D]     k_cache, v_cache [B, Hkv, max_len, D]    out [B, Hq, D]
+ *   seq_lens int32[B] on the DEVICE: sequence b attends to cache rows
+ *   0 .. seq_lens[b]-1 (the cache already holds the current token).  Values
+ *   above max_len are treated as max_len; a sequence with seq_lens[b] <= 0
+ *   gets out = 0 and lse = -inf.  Rows at or beyond seq_lens[b] are never
+ *   read.
+ *   lse [B, Hq] fp32 or NULL.
+ * Supported: dtype BF16, out_dtype BF16 or F32, D in {128, 512},
+ *   G = Hq/Hkv <= 16.
+ * Workspace: `mqa_decode_workspace_size()` bytes (chunk partials).
+ */
+size_t mqa_decode_workspace_size(int B, int Hq, int Hkv, int max_len, int head_dim);
+
+int mqa_decode(const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* seq_lens, void* out, float* lse,
+               int B, int Hq, int Hkv, int max_len, int head_dim, float scale,
+               int dtype, int out_dtype,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/* ----------------------------------------------------- MLA absorbed decode
+ * Decode for multi-head latent attention in the absorbed form.  Every cached
+ * token is one row [c_kv (512) | k_pe (64)] = 576 values shared by all heads.
+ * The caller passes the absorbed query of each head,
+ *   q_abs[b,h] = [W_UK[h] q_nope (512) | RoPE(q_rope) (64)],
+ * and applies W_UV[h] to the returned latent output itself.  The whole
+ * 576-wide row is the key; its first 512 values are the value.
+ *   q_abs [B, H, 576]   kv_cache [B, max_len, 576]   out [B, H, 512]
+ *   seq_lens int32[B] on the device, as for mqa_decode.
+ *   lse [B, H] fp32 or NULL.
+ *   scale: normally 1/sqrt(128 + 64), the original per-head q.k width.
+ * Supported: dtype BF16, out_dtype BF16 or F32, H a multiple of 16, H <= 128.
+ * Workspace: `mla_decode_workspace_size()` bytes.
+ */
+size_t mla_decode_workspace_size(int B, int H, int max_len);
+
+int mla_decode_absorbed(const void* q_abs, const void* kv_cache, const int32_t* seq_lens,
+                        void* out, float* lse, int B, int H, int max_len, float scale,
+                        int dtype, int out_dtype,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+
+#endif  /* MQA_ATTN_H */

@@ -20,9 +20,25 @@ bfloat16 tensors are kept as ``uint16`` bit patterns (what the device reads);
 
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
+
+_THREADS = max(1, min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else 4))
+
+
+def _parallel(fn, items):
+    """Run fn over items on a thread pool (numpy releases the GIL in the
+    generator and in the rounding); results are independent of the order."""
+    items = list(items)
+    if len(items) <= 1 or _THREADS == 1:
+        for it in items:
+            fn(it)
+        return
+    with ThreadPoolExecutor(max_workers=_THREADS) as ex:
+        list(ex.map(fn, items))
 
 __all__ = [
     "bf16_bits",
@@ -109,8 +125,7 @@ def prefill_inputs(B, Hq, Hkv, T, D, dtype="bf16", seed=0, d_v=None):
     out = []
     for tid, (H, dd) in enumerate(((Hq, D), (Hkv, D), (Hkv, d_v))):
         t = _store((B, H, T, dd), dtype)
-        for b in range(B):
-            _put(t, b, _draw(seed, tid, b, (H, T, dd)), dtype)
+        _parallel(lambda b: _put(t, b, _draw(seed, tid, b, (H, T, dd)), dtype), range(B))
         out.append(Tensor(t, dtype))
     return tuple(out)
 
@@ -131,7 +146,8 @@ def draw_lengths(B, lengths, L_max, seed):
 def _cache(seed, tid, B, H, L_max, D, seq_lens, dtype, nan_pad, squeeze_head=False):
     shape = (B, L_max, D) if squeeze_head else (B, H, L_max, D)
     t = _store(shape, dtype)
-    for b in range(B):
+
+    def one(b):
         L = int(seq_lens[b])
         if squeeze_head:
             _put(t, (b, slice(0, L)), _draw(seed, tid, b, (L, D)), dtype)
@@ -141,6 +157,8 @@ def _cache(seed, tid, B, H, L_max, D, seq_lens, dtype, nan_pad, squeeze_head=Fal
             _put(t, (b, slice(None), slice(0, L)), _draw(seed, tid, b, (H, L, D)), dtype)
             if L < L_max:
                 t[b, :, L:] = _nan(dtype) if nan_pad else 0
+
+    _parallel(one, range(B))
     return Tensor(t, dtype)
 
 
@@ -151,8 +169,7 @@ def decode_inputs(B, Hq, Hkv, L_max, D, dtype="bf16", seed=0, lengths=None,
     d_v = D if d_v is None else d_v
     seq_lens = draw_lengths(B, lengths, L_max, seed)
     q = _store((B, Hq, D), dtype)
-    for b in range(B):
-        _put(q, b, _draw(seed, 0, b, (Hq, D)), dtype)
+    _parallel(lambda b: _put(q, b, _draw(seed, 0, b, (Hq, D)), dtype), range(B))
     k = _cache(seed, 1, B, Hkv, L_max, D, seq_lens, dtype, nan_pad)
     v = _cache(seed, 2, B, Hkv, L_max, d_v, seq_lens, dtype, nan_pad)
     return Tensor(q, dtype), k, v, seq_lens
@@ -170,8 +187,7 @@ def mla_inputs(B, H, L_max, d_kv=576, dtype="bf16", seed=0, lengths=None,
     """q_abs [B,H,d_kv]; latent cache [B,L_max,d_kv]; seq_lens int32 [B]."""
     seq_lens = draw_lengths(B, lengths, L_max, seed)
     q = _store((B, H, d_kv), dtype)
-    for b in range(B):
-        _put(q, b, _draw(seed, 0, b, (H, d_kv)), dtype)
+    _parallel(lambda b: _put(q, b, _draw(seed, 0, b, (H, d_kv)), dtype), range(B))
     kv = _cache(seed, 1, B, 1, L_max, d_kv, seq_lens, dtype, nan_pad, squeeze_head=True)
     return Tensor(q, dtype), kv, seq_lens
 

@@ -1,0 +1,83 @@
+// CPU check of the lane/LDS index maps in csrc/layout.hpp (built with g++).
+// Prints "ok" or the first violated property and exits non-zero.
+#include <cstdio>
+#include <set>
+#include <vector>
+#include "../attention_mqa_gqa_amd/csrc/layout.hpp"
+using namespace mqa::layout;
+
+static int fail(const char* what, int a, int b) { std::printf("FAIL %s (%d, %d)\n", what, a, b); return 1; }
+
+int main() {
+    // 1. Each 32-key step: S^T rows of the two M-tiles cover keys 0..31 once,
+    //    and accumulator (mt, g, i) agrees with row 4g+i of M-tile mt.
+    for (int a = 0; a < 2; ++a) {
+        std::set<int> keys;
+        for (int h = 0; h < 2; ++h)
+            for (int m = 0; m < 16; ++m) keys.insert(st_row_key(2 * a + h, m));
+        if ((int)keys.size() != 32 || *keys.begin() != 32 * a || *keys.rbegin() != 32 * a + 31) return fail("st rows", a, 0);
+        for (int mt = 2 * a; mt < 2 * a + 2; ++mt)
+            for (int g = 0; g < 4; ++g)
+                for (int i = 0; i < 4; ++i)
+                    if (st_c_key(mt, g, i) != st_row_key(mt, 4 * g + i)) return fail("st c/row", mt, g);
+        // lane group g holds keys 8g..8g+7 of the step: the P.V contraction slots
+        for (int g = 0; g < 4; ++g)
+            for (int j = 0; j < 8; ++j)
+                if (st_c_key(2 * a + (j >> 2), g, j & 3) != 32 * a + 8 * g + j) return fail("pv slots", g, j);
+    }
+    // 2. Swizzles are bijections within a row.
+    for (int r = 0; r < 64; ++r) {
+        std::set<int> s16, s8, s4;
+        for (int c = 0; c < 64; ++c) s16.insert(c ^ kswz(r));
+        for (int c = 0; c < 8; ++c) s8.insert(c ^ swz8(r));
+        for (int c = 0; c < 4; ++c) s4.insert(c ^ swz4(r));
+        if (s16.size() != 64 || *s16.rbegin() != 63 || s8.size() != 8 || *s8.rbegin() != 7 || s4.size() != 4 || *s4.rbegin() != 3)
+            return fail("bijection", r, 0);
+    }
+    // 3. Bank slots (16-byte units mod 256 bytes) are distinct over the 16
+    //    lanes of one lane group for every operand read.
+    for (int rowbytes : {256, 1024, 1152 - 128}) {   // K tile rows (D = 128, 512; MLA latent 512)
+        for (int mt = 0; mt < 4; ++mt)
+            for (int ks = 0; ks < rowbytes / 64; ++ks)
+                for (int g = 0; g < 4; ++g) {
+                    std::set<int> slots;
+                    for (int m = 0; m < 16; ++m) {
+                        int kk = st_row_key(mt, m);
+                        int pos = (4 * ks + g) ^ kswz(kk);
+                        long addr = (long)kk * rowbytes + pos * 16;
+                        slots.insert((int)((addr / 16) % 16));
+                    }
+                    if (slots.size() != 16) return fail("K reads", rowbytes, ks);
+                }
+    }
+    for (int mt = 0; mt < 4; ++mt)       // 128-byte rows (MLA RoPE part)
+        for (int g = 0; g < 4; ++g)
+            for (int ks = 0; ks < 2; ++ks) {
+                std::set<int> slots;
+                for (int m = 0; m < 16; ++m) {
+                    int kk = st_row_key(mt, m);
+                    long addr = (long)kk * 128 + (((4 * ks + g) ^ swz8(kk)) * 16);
+                    slots.insert((int)((addr / 16) % 16));
+                }
+                if (slots.size() != 16) return fail("rope reads", mt, g);
+            }
+    for (int rl : {4, 8})                 // V^T rows of rl chunks
+        for (int mt = 0; mt < 32; ++mt)
+            for (int kp = 0; kp < rl / 4; ++kp)
+                for (int g = 0; g < 4; ++g) {
+                    std::set<int> slots;
+                    for (int m = 0; m < 16; ++m) {
+                        int d = pv_row_d(mt, m);
+                        long addr = ((long)d * rl + ((4 * kp + g) ^ vswz(d, rl))) * 16;
+                        slots.insert((int)((addr / 16) % 16));
+                    }
+                    if (slots.size() != 16) return fail("V reads", rl, mt);
+                }
+    // 4. Output columns: accumulators (2b, g, 0..3) and (2b+1, g, 0..3) are 8 consecutive dims.
+    for (int b = 0; b < 16; ++b)
+        for (int g = 0; g < 4; ++g)
+            for (int j = 0; j < 8; ++j)
+                if (pv_c_d(2 * b + (j >> 2), g, j & 3) != 32 * b + 8 * g + j) return fail("out cols", b, g);
+    std::printf("ok\n");
+    return 0;
+}

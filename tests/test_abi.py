@@ -1,0 +1,124 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+the header declares, and rejects bad arguments on the host (before any HIP
+call) with the documented status codes."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mqa_attn.h")
+
+mqa = pytest.importorskip("attention_mqa_gqa_amd")
+lib = mqa.lib
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+F32, BF16 = 0, 1
+P = ctypes.c_void_p(4096)          # a 16-byte aligned stand-in: never dereferenced on these paths
+MIS = ctypes.c_void_p(4096 + 8)    # misaligned
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\**\s+\**([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_functions_are_exported():
+    names = _declared_functions()
+    assert len(names) == 9, names
+    assert sorted(names) == sorted(mqa.EXPORTED_SYMBOLS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings():
+    assert lib.mqa_attn_abi_version() == 1
+    for s in (OK, INVALID, UNSUPPORTED, WORKSPACE, -4, 7):
+        assert lib.mqa_status_string(s)
+    assert lib.mqa_last_hip_error_name() == b"hipSuccess"
+
+
+def _prefill(q=P, k=P, v=P, out=P, lse=None, B=1, Hq=16, Hkv=1, T=128, D=512, scale=0.05, causal=1,
+             din=BF16, dout=BF16, ws=P, wsb=1 << 40):
+    return lib.mqa_prefill(q, k, v, out, lse, B, Hq, Hkv, T, D, scale, causal, din, dout, ws, wsb, None)
+
+
+def test_prefill_rejections():
+    assert _prefill(Hkv=3) == INVALID                    # Hq % Hkv
+    assert _prefill(B=-1) == INVALID
+    assert _prefill(T=-5) == INVALID
+    assert _prefill(Hq=0) == INVALID
+    assert _prefill(scale=float("inf")) == INVALID
+    assert _prefill(scale=float("nan")) == INVALID
+    assert _prefill(din=7) == INVALID
+    assert _prefill(q=None) == INVALID
+    assert _prefill(out=MIS) == INVALID
+    assert _prefill(lse=ctypes.c_void_p(4098)) == INVALID
+    assert _prefill(D=256) == UNSUPPORTED                # bf16: D in {128, 512}
+    assert _prefill(D=512, Hq=256, Hkv=1) == UNSUPPORTED  # group larger than a workgroup's rows
+    assert _prefill(din=F32, dout=BF16) == UNSUPPORTED
+    assert _prefill(din=F32, dout=F32, D=100) == UNSUPPORTED
+    assert _prefill(ws=None, wsb=0) == WORKSPACE
+    need = lib.mqa_prefill_workspace_size(1, 16, 1, 128, 512, BF16)
+    assert _prefill(wsb=need - 1) == WORKSPACE
+    assert _prefill(ws=MIS, wsb=need) == INVALID
+
+
+def test_prefill_empty_calls_are_ok():
+    assert _prefill(B=0, q=None, k=None, v=None, out=None) == OK
+    assert _prefill(T=0, q=None, k=None, v=None, out=None) == OK
+
+
+def test_prefill_workspace_size():
+    # bf16: a tiled transposed copy of V padded to whole 32-key tiles
+    assert lib.mqa_prefill_workspace_size(2, 16, 1, 4096, 512, BF16) == 2 * 1 * 4096 * 512 * 2
+    assert lib.mqa_prefill_workspace_size(1, 8, 2, 33, 128, BF16) == 1 * 2 * 64 * 128 * 2
+    assert lib.mqa_prefill_workspace_size(1, 16, 1, 128, 512, F32) == 0
+
+
+def _decode(q=P, k=P, v=P, sl=P, out=P, lse=None, B=64, Hq=16, Hkv=1, L=8192, D=512, scale=0.05,
+            dt=BF16, dout=BF16, ws=P, wsb=1 << 40):
+    return lib.mqa_decode(q, k, v, sl, out, lse, B, Hq, Hkv, L, D, scale, dt, dout, ws, wsb, None)
+
+
+def test_decode_rejections():
+    assert _decode(Hkv=3) == INVALID
+    assert _decode(sl=None) == INVALID
+    assert _decode(sl=ctypes.c_void_p(4098)) == INVALID
+    assert _decode(L=0) == INVALID
+    assert _decode(dt=F32, dout=F32) == UNSUPPORTED
+    assert _decode(D=256) == UNSUPPORTED
+    assert _decode(Hq=64, Hkv=2) == UNSUPPORTED          # group of 32 > 16 MFMA columns
+    assert _decode(ws=None) == WORKSPACE
+    need = lib.mqa_decode_workspace_size(64, 16, 1, 8192, 512)
+    assert need > 0
+    assert _decode(wsb=need - 4) == WORKSPACE
+    assert _decode(B=0, q=None) == OK
+
+
+def _mla(q=P, kv=P, sl=P, out=P, lse=None, B=32, H=128, L=32768, scale=0.072, dt=BF16, dout=BF16,
+         ws=P, wsb=1 << 40):
+    return lib.mla_decode_absorbed(q, kv, sl, out, lse, B, H, L, scale, dt, dout, ws, wsb, None)
+
+
+def test_mla_rejections():
+    assert _mla(H=0) == INVALID
+    assert _mla(kv=MIS) == INVALID
+    assert _mla(H=24) == UNSUPPORTED
+    assert _mla(H=256) == UNSUPPORTED
+    assert _mla(dt=F32) == UNSUPPORTED
+    assert _mla(ws=None) == WORKSPACE
+    need = lib.mla_decode_workspace_size(32, 128, 32768)
+    assert _mla(wsb=need - 1) == WORKSPACE
+    assert _mla(B=0, q=None) == OK
+
+
+def test_decode_workspace_grows_with_splits():
+    a = lib.mqa_decode_workspace_size(64, 16, 1, 8192, 512)
+    b = lib.mqa_decode_workspace_size(64, 16, 1, 32768, 512)
+    assert b >= a > 0
+    # partials: (D + 2) floats per (sequence, head, split)
+    assert a % (64 * 16 * (512 + 2) * 4) == 0

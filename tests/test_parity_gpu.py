@@ -1,0 +1,271 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Inputs come from the seeded synthetic generator; the oracle reads the same
+bf16-rounded values the device gets, upcast exactly.  Bars: max |err| <=
+2e-2 for bf16 inputs, <= 1e-5 for fp32 (both on outputs and on the
+natural-log LSE).  Small cases are compared element by element; the
+full-size workloads (in the launch configuration the bench times) are
+compared on sampled rows / sequences that the oracle recomputes one by one.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from synthetic import (decode_inputs, decode_slice, mla_inputs, mla_slice, prefill_inputs,
+                       round_bf16, draw_lengths)
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 2e-2
+F32_TOL = 1e-5
+
+
+def _say(msg):
+    print(f"\n[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as _t
+    if not _t.cuda.is_available():
+        pytest.skip("no GPU")
+    return _t
+
+
+@pytest.fixture(scope="module")
+def mqa():
+    import attention_mqa_gqa_amd as m
+    return m
+
+
+def dev(torch, t):
+    """synthetic.Tensor -> device tensor with identical bits."""
+    if t.dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(t.data).view(np.int16)).to("cuda").view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(t.data)).to("cuda")
+
+
+def host(x):
+    return x.float().cpu().numpy().astype(np.float64)
+
+
+def _maxerr(a, b):
+    return float(np.max(np.abs(np.asarray(a, dtype=np.float64) - np.asarray(b, dtype=np.float64))))
+
+
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+
+def test_prefill_f32_mqa_t128_full(torch, mqa):
+    """fp32 MQA prefill B=1, Hq=16, Hkv=1, T=128, D=512, causal: every element."""
+    _say("prefill f32 B1 Hq16 Hkv1 T128 D512")
+    q, k, v = prefill_inputs(1, 16, 1, 128, 512, "f32", seed=0)
+    lse = torch.empty((1, 16, 128), dtype=torch.float32, device="cuda")
+    out = mqa.mqa_prefill(dev(torch, q), dev(torch, k), dev(torch, v), causal=True, lse=lse)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.prefill_ref(q.f32(), k.f32(), v.f32(), 1 / math.sqrt(512), True)
+    assert _maxerr(host(out), ref) <= F32_TOL
+    assert _maxerr(host(lse), ref_lse) <= F32_TOL
+
+
+PREFILL_SMALL = [
+    # B, Hq, Hkv, T, D, causal, out dtype
+    (2, 16, 1, 200, 512, True, "bf16"),
+    (1, 16, 1, 200, 512, False, "f32"),
+    (1, 16, 2, 129, 128, True, "f32"),
+    (1, 8, 8, 77, 128, True, "bf16"),
+    (1, 64, 8, 150, 128, True, "bf16"),
+    (2, 4, 1, 1, 512, True, "bf16"),
+    (1, 32, 1, 40, 128, True, "bf16"),
+    (1, 128, 1, 20, 512, True, "f32"),
+    (1, 12, 4, 65, 128, False, "bf16"),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,D,causal,odt", PREFILL_SMALL)
+def test_prefill_bf16_small(torch, mqa, B, Hq, Hkv, T, D, causal, odt):
+    _say(f"prefill bf16 B{B} Hq{Hq} Hkv{Hkv} T{T} D{D} causal={causal} out={odt}")
+    q, k, v = prefill_inputs(B, Hq, Hkv, T, D, "bf16", seed=1)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device="cuda")
+    out_dtype = torch.float32 if odt == "f32" else torch.bfloat16
+    out = mqa.mqa_prefill(dev(torch, q), dev(torch, k), dev(torch, v), causal=causal, lse=lse,
+                          out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.prefill_ref(q.f32(), k.f32(), v.f32(), 1 / math.sqrt(D), causal)
+    assert np.all(np.isfinite(host(out)))
+    assert _maxerr(host(out), ref) <= BF16_TOL
+    assert _maxerr(host(lse), ref_lse) <= BF16_TOL
+
+
+def test_prefill_f32_ragged_and_gqa(torch, mqa):
+    _say("prefill f32 B2 Hq6 Hkv3 T37 D128 causal + full")
+    q, k, v = prefill_inputs(2, 6, 3, 37, 128, "f32", seed=2)
+    for causal in (True, False):
+        out = mqa.mqa_prefill(dev(torch, q), dev(torch, k), dev(torch, v), causal=causal, scale=0.3)
+        torch.cuda.synchronize()
+        ref, _ = oracle.prefill_ref(q.f32(), k.f32(), v.f32(), 0.3, causal)
+        assert _maxerr(host(out), ref) <= F32_TOL
+
+
+def _sample_rows(B, H, T, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = [(0, 0, 0), (B - 1, H - 1, T - 1), (0, H - 1, T - 1), (B - 1, 0, 1)]
+    rows += [(int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(T))) for _ in range(n)]
+    return rows
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,D", [(2, 16, 1, 4096, 512), (1, 64, 8, 8192, 128)])
+def test_prefill_bf16_full_size_sampled(torch, mqa, B, Hq, Hkv, T, D):
+    """Full-size prefill (MQA d=512 T=4096 B=2; GQA 64/8 d=128 T=8192), causal,
+    in the bench's launch configuration; sampled rows vs the oracle, plus
+    bitwise run-to-run repeatability."""
+    _say(f"prefill bf16 full B{B} Hq{Hq} Hkv{Hkv} T{T} D{D}")
+    q, k, v = prefill_inputs(B, Hq, Hkv, T, D, "bf16", seed=0)
+    dq, dk, dv = dev(torch, q), dev(torch, k), dev(torch, v)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device="cuda")
+    out = mqa.mqa_prefill(dq, dk, dv, causal=True, lse=lse)
+    out2 = mqa.mqa_prefill(dq, dk, dv, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    rows = _sample_rows(B, Hq, T, 40, seed=5)
+    ref, ref_lse = oracle.prefill_rows_ref(q.f32(), k.f32(), v.f32(), rows, 1 / math.sqrt(D), True)
+    got = np.stack([host(out[b, h, i]) for b, h, i in rows])
+    got_lse = np.array([float(lse[b, h, i]) for b, h, i in rows])
+    assert _maxerr(got, ref) <= BF16_TOL
+    assert _maxerr(got_lse, ref_lse) <= BF16_TOL
+    assert bool(torch.isfinite(out.float()).all())
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+
+DECODE_SMALL = [
+    # B, Hq, Hkv, L_max, D, lengths, out dtype
+    (5, 16, 1, 3000, 512, [1, 17, 2048, 2049, 3000], "bf16"),
+    (4, 64, 8, 5000, 128, [1, 1023, 1024, 5000], "f32"),
+    (3, 8, 8, 700, 128, [700, 3, 64], "bf16"),
+    (2, 12, 3, 300, 512, [299, 300], "f32"),
+    (3, 16, 16, 100, 128, [1, 2, 100], "bf16"),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,L,D,lengths,odt", DECODE_SMALL)
+def test_decode_small(torch, mqa, B, Hq, Hkv, L, D, lengths, odt):
+    _say(f"decode B{B} Hq{Hq} Hkv{Hkv} L{L} D{D} lens={lengths} out={odt}")
+    q, kc, vc, sl = decode_inputs(B, Hq, Hkv, L, D, "bf16", seed=3, lengths=lengths)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    out_dtype = torch.float32 if odt == "f32" else torch.bfloat16
+    out = mqa.mqa_decode(dev(torch, q), dev(torch, kc), dev(torch, vc), torch.from_numpy(sl).cuda(),
+                         lse=lse, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.decode_ref(q.f32(), kc.f32(), vc.f32(), sl, 1 / math.sqrt(D))
+    assert np.all(np.isfinite(host(out)))
+    assert _maxerr(host(out), ref) <= BF16_TOL
+    assert _maxerr(host(lse), ref_lse) <= BF16_TOL
+
+
+def test_decode_zero_length_and_repeatability(torch, mqa):
+    _say("decode zero-length rows, repeatability")
+    q, kc, vc, sl = decode_inputs(3, 16, 1, 4500, 512, "bf16", seed=4, lengths=[4500, 1, 2500])
+    dsl = torch.tensor([4500, 0, 2500], dtype=torch.int32, device="cuda")
+    args = (dev(torch, q), dev(torch, kc), dev(torch, vc), dsl)
+    lse = torch.empty((3, 16), dtype=torch.float32, device="cuda")
+    out = mqa.mqa_decode(*args, lse=lse)
+    out2 = mqa.mqa_decode(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    assert float(out[1].float().abs().max()) == 0.0
+    assert bool(torch.isinf(lse[1]).all()) and float(lse[1].max()) < 0
+    ref, _ = oracle.decode_ref(q.f32()[[0, 2]], kc.f32()[[0, 2]], vc.f32()[[0, 2]], np.array([4500, 2500]),
+                               1 / math.sqrt(512))
+    assert _maxerr(host(out[[0, 2]]), ref) <= BF16_TOL
+
+
+def _decode_full_check(torch, mqa, B, Hq, Hkv, L, D, lengths, samples):
+    q, kc, vc, sl = decode_inputs(B, Hq, Hkv, L, D, "bf16", seed=0, lengths=lengths)
+    dq, dk, dv = dev(torch, q), dev(torch, kc), dev(torch, vc)
+    del kc, vc
+    dsl = torch.from_numpy(sl).cuda()
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    out = mqa.mqa_decode(dq, dk, dv, dsl, lse=lse)
+    out2 = mqa.mqa_decode(dq, dk, dv, dsl)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    assert bool(torch.isfinite(out.float()).all())
+    for b in samples:
+        Lb = int(sl[b])
+        qs, ks, vs = decode_slice(0, b, Hq, Hkv, Lb, D)
+        ref, ref_lse = oracle.decode_ref(round_bf16(qs)[None], round_bf16(ks)[None], round_bf16(vs)[None],
+                                         np.array([Lb]), 1 / math.sqrt(D))
+        assert _maxerr(host(out[b]), ref[0]) <= BF16_TOL
+        assert _maxerr(host(lse[b]), ref_lse[0]) <= BF16_TOL
+
+
+def test_decode_full_size_mqa(torch, mqa):
+    """MQA decode batch 64, Hq=16, Hkv=1, d=512, cache 8192 (bench configuration)."""
+    _say("decode full B64 Hq16 Hkv1 L8192 D512")
+    _decode_full_check(torch, mqa, 64, 16, 1, 8192, 512, None, samples=[0, 17, 63])
+
+
+def test_decode_full_size_gqa(torch, mqa):
+    """GQA decode batch 128, Hq=64, Hkv=8, d=128, lengths U[1024, 16384]."""
+    _say("decode full B128 Hq64 Hkv8 L16384 D128 lengths U[1024,16384]")
+    sl = draw_lengths(128, (1024, 16384), 16384, 0)
+    samples = [0, int(np.argmin(sl)), int(np.argmax(sl)), 127]
+    _decode_full_check(torch, mqa, 128, 64, 8, 16384, 128, (1024, 16384), samples)
+
+
+# ---------------------------------------------------------------------------
+# MLA absorbed decode
+# ---------------------------------------------------------------------------
+
+MLA_SMALL = [
+    # B, H, L_max, lengths, out dtype
+    (3, 128, 2000, [1, 999, 2000], "bf16"),
+    (2, 16, 300, [300, 33], "f32"),
+    (2, 64, 1100, [1100, 1025], "bf16"),
+]
+
+
+@pytest.mark.parametrize("B,H,L,lengths,odt", MLA_SMALL)
+def test_mla_small(torch, mqa, B, H, L, lengths, odt):
+    _say(f"mla B{B} H{H} L{L} lens={lengths} out={odt}")
+    q, kv, sl = mla_inputs(B, H, L, 576, "bf16", seed=6, lengths=lengths)
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    out_dtype = torch.float32 if odt == "f32" else torch.bfloat16
+    out = mqa.mla_decode_absorbed(dev(torch, q), dev(torch, kv), torch.from_numpy(sl).cuda(), lse=lse,
+                                  out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    scale = 1 / math.sqrt(192)
+    ref, ref_lse = oracle.mla_absorbed_ref(q.f32(), kv.f32(), sl, scale)
+    assert np.all(np.isfinite(host(out)))
+    assert _maxerr(host(out), ref) <= BF16_TOL
+    assert _maxerr(host(lse), ref_lse) <= BF16_TOL
+
+
+def test_mla_full_size(torch, mqa):
+    """MLA absorbed decode batch 32, H=128, context 32768, scale 1/sqrt(192)."""
+    _say("mla full B32 H128 L32768")
+    B, H, L = 32, 128, 32768
+    q, kv, sl = mla_inputs(B, H, L, 576, "bf16", seed=0)
+    dq, dkv = dev(torch, q), dev(torch, kv)
+    del kv
+    dsl = torch.from_numpy(sl).cuda()
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    out = mqa.mla_decode_absorbed(dq, dkv, dsl, lse=lse)
+    out2 = mqa.mla_decode_absorbed(dq, dkv, dsl)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    scale = 1 / math.sqrt(192)
+    for b in (0, 31):
+        qs, kvs = mla_slice(0, b, H, L)
+        ref, ref_lse = oracle.mla_absorbed_ref(round_bf16(qs)[None], round_bf16(kvs)[None], np.array([L]), scale)
+        assert _maxerr(host(out[b]), ref[0]) <= BF16_TOL
+        assert _maxerr(host(lse[b]), ref_lse[0]) <= BF16_TOL
