@@ -62,6 +62,11 @@ class MqaError(RuntimeError):
 
 
 def _load():
+    # torch ships its own HIP runtime (soname libamdhip64.so.7).  Load it first
+    # so the library binds to that same runtime: with two runtimes in one
+    # process ours would not see the device, and torch's stream handles would
+    # not belong to the runtime we launch on.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python attention_mqa_gqa_amd/build.py`")
     l = ctypes.CDLL(LIB_PATH)
