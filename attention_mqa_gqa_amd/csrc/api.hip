@@ -65,7 +65,7 @@ size_t mqa_prefill_workspace_size(int B, int Hq, int Hkv, int T, int head_dim, i
     const mqa::PrefillPlan p = mqa::prefill_plan(head_dim, 1);
     if (p.kt <= 0) return 0;
     const size_t tiles = ((size_t)T + p.kt - 1) / p.kt;
-    return (size_t)B * Hkv * tiles * p.kt * head_dim * 2;
+    return (size_t)B * Hkv * tiles * p.kt * head_dim * 2 * 2;   // K tile + V^T tile, bf16
 }
 
 int mqa_prefill(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv, int T,

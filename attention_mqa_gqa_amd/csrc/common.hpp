@@ -6,6 +6,9 @@
 //   A/B of v_mfma_f32_16x16x32_bf16 (8 bf16 per lane): lane l holds
 //        A[l % 16][k] / B[k][l % 16] for the 8 k of lane group g = l/16.
 //   A/B of v_mfma_f32_16x16x16_bf16 (4 bf16 per lane): the 4 k of group g.
+//   v_mfma_f32_32x32x16_bf16: A/B lane l holds row/column l % 32 and 8 k of
+//        lane half l/32; C (f32x16): accumulator i of lane l is
+//        C[8*(i/4) + 4*(l/32) + i%4][l % 32].
 // The kernels only rely on A and B sharing one (group, slot) -> k map, so a
 // contraction pairs A slot j of group g with B slot j of group g.
 #pragma once
@@ -19,6 +22,7 @@ typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -34,6 +38,26 @@ constexpr float kRescaleSlack = 8.0f;
 
 __device__ __forceinline__ f32x4 mfma_16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma_32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// acc *= alpha for an accumulator tile that lives in AGPRs, one register at
+// a time through a temporary VGPR.  Written out so that the rare rescale of
+// the output accumulators does not make the compiler move them into VGPRs.
+__device__ __forceinline__ void scale_acc(f32x16& acc, float alpha) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        float t;
+        asm volatile(
+            "v_accvgpr_read_b32 %1, %0\n\t"
+            "v_mul_f32 %1, %1, %2\n\t"
+            "v_accvgpr_write_b32 %0, %1"
+            : "+a"(acc[i]), "=&v"(t)
+            : "v"(alpha));
+    }
 }
 
 __device__ __forceinline__ f32x4 mfma_16x16x16(const u32x2& a, const u32x2& b, const f32x4& c) {
@@ -71,6 +95,11 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
 }
 constexpr uint32_t kSelLoHalves = 0x05040100u;  // {lo.h0, hi.h0}
 constexpr uint32_t kSelHiHalves = 0x07060302u;  // {lo.h1, hi.h1}
+
+// Max / sum over the two lane halves l, l^32 (the two halves holding one
+// output column of a 32x32 MFMA tile).
+__device__ __forceinline__ float max_over_halves(float v) { return fmaxf(v, __shfl_xor(v, 32)); }
+__device__ __forceinline__ float sum_over_halves(float v) { return v + __shfl_xor(v, 32); }
 
 // Max / sum over the four lanes l, l^16, l^32, l^48 (the four lane groups
 // that share one MFMA output column).

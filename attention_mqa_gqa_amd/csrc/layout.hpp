@@ -50,5 +50,29 @@ MQA_HD constexpr int swz4(int row) { return (row >> 3) & 3; }
 // Swizzle for a transposed V tile row (head dim d) holding rl chunks of keys.
 MQA_HD constexpr int vswz(int d, int rl) { return rl == 4 ? swz4(d) : swz8(d); }
 
+// ---------------------------------------------------------------------------
+// Maps for v_mfma_f32_32x32x16_bf16 (A/B: lane l holds row/column l % 32 and
+// 8 contraction elements of lane half l / 32; C: accumulator i of lane l is
+// row 8*(i/4) + 4*(l/32) + i%4, column l % 32).
+//
+// Row m of a 32-row A operand is mapped to key / head dim swap23(m) (bits 2
+// and 3 exchanged).  Then the 16 accumulators of lane half h are the keys
+// 8h..8h+7 (i = 0..7) and 16+8h..16+8h+7 (i = 8..15): the scores of a lane
+// are directly the two 16-key P operands of the next MFMA, and a P.V output
+// lane holds two runs of 8 consecutive head dims.
+MQA_HD constexpr int swap23(int m) { return (m & ~12) | (((m >> 2) & 1) << 3) | (((m >> 3) & 1) << 2); }
+// key (head dim) held by accumulator i of lane half h
+MQA_HD constexpr int c32_index(int h, int i) { return 16 * (i >> 3) + 8 * h + (i & 7); }
+
+// Swizzles for 32-row operand reads (16 lanes -> 16 distinct 16-byte slots
+// per 256 bytes and 8 lanes -> 8 distinct slots per 128 bytes):
+//   rows of >= 16 chunks, rows of 8 chunks, rows of 4 chunks.
+MQA_HD constexpr int swz32_16(int r) { return swap23(r & 15); }
+MQA_HD constexpr int swz32_8(int r) { return ((r >> 1) & 1) | (((r >> 3) & 1) << 1) | (((r ^ (r >> 2)) & 1) << 2); }
+MQA_HD constexpr int swz32_4(int r) { return ((r >> 3) & 1) | ((((r >> 1) ^ (r >> 2)) & 1) << 1); }
+MQA_HD constexpr int swz32(int r, int row_chunks) {
+    return row_chunks >= 16 ? swz32_16(r) : (row_chunks == 8 ? swz32_8(r) : swz32_4(r));
+}
+
 }  // namespace layout
 }  // namespace mqa

@@ -24,18 +24,38 @@
 namespace mqa {
 
 // ---------------------------------------------------------------------------
-// V [B*Hkv, T, D] -> Vt tiles [B*Hkv, n_tiles, D rows of KT keys] in exactly
-// the swizzled order the prefill kernel keeps in LDS (zero past T).
+// K, V [B*Hkv, T, D] -> tile stream [B*Hkv, n_tiles, (K tile | V^T tile)].
+// Each 32-key tile is stored exactly as the prefill kernel keeps it in LDS:
+// the K tile row-major (row = key) and the V^T tile (row = head dim, 32 keys
+// per row), both with 16-byte chunks in swizzled order, zero past T.  V's
+// contraction index (the key) is its row index, so the P.V operand needs it
+// transposed; doing that here once, and storing both tiles contiguously,
+// turns every global->LDS copy of the main kernel into a straight 16-byte
+// stream (uniform base + 16 * lane).
 // ---------------------------------------------------------------------------
 template <int D, int KT>
-__global__ __launch_bounds__(256) void vt_pack_kernel(const bf16* __restrict__ V, bf16* __restrict__ Vt,
-                                                      int T, int n_tiles) {
+__global__ __launch_bounds__(256) void kv_pack_kernel(const bf16* __restrict__ K, const bf16* __restrict__ V,
+                                                      bf16* __restrict__ KVt, int T, int n_tiles) {
     constexpr int RL = KT / 8;           // 16-byte chunks per V^T row
-    constexpr int NB = RL * (D / 8);     // 8x8 blocks per tile
+    constexpr int ROW_CHUNKS = D / 8;    // 16-byte chunks per K row
+    constexpr int NB = RL * (D / 8);     // 8x8 blocks per V tile
+    constexpr int TILE = KT * D;
     const int tile = blockIdx.x;
     const size_t bh = blockIdx.y;
-    const bf16* src = V + bh * (size_t)T * D;
-    bf16* dst = Vt + (bh * n_tiles + tile) * (size_t)(KT * D);
+    const bf16* ksrc = K + bh * (size_t)T * D;
+    const bf16* vsrc = V + bh * (size_t)T * D;
+    bf16* kdst = KVt + (bh * n_tiles + tile) * (size_t)(2 * TILE);
+    bf16* vdst = kdst + TILE;
+    // K tile: chunk position p of row kk holds global chunk p ^ swz(kk)
+    for (int q = threadIdx.x; q < KT * ROW_CHUNKS; q += 256) {
+        const int kk = q / ROW_CHUNKS;
+        const int p = q % ROW_CHUNKS;
+        const int c = p ^ layout::swz32(kk, ROW_CHUNKS);
+        const int key = tile * KT + kk;
+        const u32x4 val = key < T ? ldg16(ksrc + (size_t)key * D + c * 8) : u32x4{0, 0, 0, 0};
+        *(u32x4*)(kdst + (size_t)q * 8) = val;
+    }
+    // V^T tile: 8x8 blocks transposed with byte permutes
     for (int blk = threadIdx.x; blk < NB; blk += 256) {
         const int kb = blk % RL;
         const int db = blk / RL;
@@ -43,7 +63,7 @@ __global__ __launch_bounds__(256) void vt_pack_kernel(const bf16* __restrict__ V
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int key = tile * KT + kb * 8 + j;
-            if (key < T) r[j] = ldg16(src + (size_t)key * D + db * 8);
+            if (key < T) r[j] = ldg16(vsrc + (size_t)key * D + db * 8);
             else r[j] = u32x4{0, 0, 0, 0};
         }
 #pragma unroll
@@ -56,116 +76,105 @@ __global__ __launch_bounds__(256) void vt_pack_kernel(const bf16* __restrict__ V
             o.y = perm(r[3][w], r[2][w], sel);
             o.z = perm(r[5][w], r[4][w], sel);
             o.w = perm(r[7][w], r[6][w], sel);
-            const int pos = kb ^ layout::vswz(d, RL);
-            *(u32x4*)(dst + (size_t)(d * RL + pos) * 8) = o;
+            const int pos = kb ^ layout::swz32(d, RL);
+            *(u32x4*)(vdst + (size_t)(d * RL + pos) * 8) = o;
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// bf16 flash prefill.
-//   D      head dim (128 or 512)          NT  16-row N-tiles per row block
-//   NW     waves per workgroup            KT  keys per tile (multiple of 32)
-//   SPLIT  waves sharing one row block; each owns D/SPLIT head dims of both
-//          the Q.K^T contraction (fp32 partial scores are summed through
-//          LDS) and of the output accumulator, which halves the registers a
-//          wave needs at D = 512 without changing the LDS traffic per row.
-// Rows of a workgroup: r = 0 .. (NW/SPLIT)*16*NT-1, head = r % G,
-// token = t0 + r / G.
+// bf16 flash prefill on v_mfma_f32_32x32x16_bf16.
+//   D   head dim (128 or 512)        NR  32-row N-tiles per wave
+//   NW  waves per workgroup          KT  keys per tile (32)
+// Each wave owns 32*NR query rows with the full head dim: Q^T operands and
+// the O^T accumulator stay in registers for the whole key loop (one wave per
+// SIMD at D = 512).  Rows of a workgroup: r = 0 .. NW*32*NR-1, head = r % G,
+// token = t0 + r / G.  Keys inside a tile follow layout::swap23 so that the
+// score accumulators are the P operands of the P.V MFMA as they stand.
 // ---------------------------------------------------------------------------
-template <int D, int NT, int NW, int KT, int SPLIT, bool CAUSAL, bool OUT_F32>
+template <int D, int NR, int NW, int KT, bool CAUSAL, bool OUT_F32>
 __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ Vt,
+    const bf16* __restrict__ Q, const bf16* __restrict__ KVt,
     void* __restrict__ Out, float* __restrict__ Lse, int Hq, int Hkv, int T, int G,
     int tok_per_wg, int n_tok_blocks, int n_kv_tiles, float scale_log2) {
-    constexpr int RW = 16 * NT;
-    constexpr int DS = D / SPLIT;         // head dims owned by one wave
-    constexpr int KS = DS / 32;           // QK^T contraction steps per wave
-    constexpr int MT_S = KT / 16;         // S^T M-tiles (keys)
-    constexpr int MT_O = DS / 16;         // O^T M-tiles (head dims)
-    constexpr int KS_P = KT / 32;         // P.V contraction steps
+    constexpr int RW = 32 * NR;           // rows per wave
+    constexpr int KS = D / 16;            // QK^T contraction steps
+    constexpr int MT_O = D / 32;          // O^T M-tiles (head dims)
+    constexpr int KSP = KT / 16;          // P.V contraction steps
     constexpr int RL = KT / 8;            // chunks per V^T row
     constexpr int TILE = KT * D;          // elements per K tile (and per V^T tile)
-    constexpr int CHUNKS = TILE / 8;
-    constexpr int LOADS = CHUNKS / (NW * 64);
+    constexpr int LOADS = 2 * TILE / 8 / (NW * 64);   // 16-byte copies per thread per tile
     constexpr int ROW_CHUNKS = D / 8;
-    constexpr int NSX = MT_S * NT;        // f32x4 partial-score registers per lane
-    static_assert(CHUNKS % (NW * 64) == 0, "tile must split evenly over the waves");
-    static_assert(DS % 128 == 0 || DS == D, "split head dim");
-    static_assert(KT % 32 == 0 && (RL == 4 || RL == 8), "key tile");
-    static_assert(SPLIT == 1 || NW * 64 * NSX * 16 <= TILE * 2, "score exchange must fit in a K tile");
+    static_assert(KT == 32, "key tile");
+    static_assert((2 * TILE / 8) % (NW * 64) == 0, "tile must split evenly over the waves");
 
     __shared__ __attribute__((aligned(16))) bf16 smem[2 * 2 * TILE];
 
     const int lane = lane_id();
     const int w = wave_id();
-    const int g = lane >> 4;
-    const int n = lane & 15;
-    const int rb = w / SPLIT;             // row block of this wave
-    const int hd = w % SPLIT;             // head-dim part of this wave
-    const int dbase = hd * DS;
+    const int h2 = lane >> 5;             // lane half
+    const int n = lane & 31;              // row (column of the 32x32 tile)
     const int tb = CAUSAL ? (n_tok_blocks - 1 - (int)blockIdx.x) : (int)blockIdx.x;
     const int hk = blockIdx.y;
     const int b = blockIdx.z;
     const int t0 = tb * tok_per_wg;
     const int rows_used = tok_per_wg * G;
 
-    int row_tok[NT];
-    int row_head[NT];
-    bool row_ok[NT];
+    int row_tok[NR];
+    int row_head[NR];
+    bool row_ok[NR];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        const int r = rb * RW + 16 * nt + n;
+    for (int nt = 0; nt < NR; ++nt) {
+        const int r = w * RW + 32 * nt + n;
         row_tok[nt] = t0 + r / G;
         row_head[nt] = hk * G + r % G;
         row_ok[nt] = (r < rows_used) && (row_tok[nt] < T);
     }
+    int wave_tok_min = t0 + (w * RW) / G;      // smallest token among this wave's rows
 
-    // Q^T operands (B of S^T): lane group g holds head dims dbase + 32ks + 8g .. +7.
-    bf16x8 qb[NT][KS];
+    // Q^T operands: lane half h2 holds head dims 16ks + 8h2 .. +7 of row n.
+    bf16x8 qb[NR][KS];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        const bf16* qrow = Q + (((size_t)b * Hq + row_head[nt]) * T + (row_ok[nt] ? row_tok[nt] : 0)) * D + dbase;
+    for (int nt = 0; nt < NR; ++nt) {
+        const bf16* qrow = Q + (((size_t)b * Hq + row_head[nt]) * T + (row_ok[nt] ? row_tok[nt] : 0)) * D;
         const u32x4 zero = {0, 0, 0, 0};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const u32x4 v = ldg16(qrow + 32 * ks + 8 * g);
+            const u32x4 v = ldg16(qrow + 16 * ks + 8 * h2);
             qb[nt][ks] = __builtin_bit_cast(bf16x8, row_ok[nt] ? v : zero);
         }
     }
 
     const size_t bh = (size_t)b * Hkv + hk;
-    const bf16* Kbh = K + bh * (size_t)T * D;
-    const bf16* Vtbh = Vt + bh * (size_t)n_kv_tiles * TILE;
+    const bf16* KVbh = KVt + bh * (size_t)n_kv_tiles * 2 * TILE;
 
     const int t_last = min(T, t0 + tok_per_wg) - 1;
     const int n_tiles = CAUSAL ? (t_last / KT + 1) : n_kv_tiles;
 
+    // tile `tile` of the packed stream -> LDS stage: a straight contiguous copy
     auto issue = [&](int tile, int stage) {
-        bf16* ks_lds = smem + stage * 2 * TILE;
-        bf16* vs_lds = ks_lds + TILE;
-        const bf16* Vtile = Vtbh + (size_t)tile * TILE;
+        const bf16* src = KVbh + (size_t)tile * 2 * TILE;
+        bf16* dst = smem + stage * 2 * TILE;
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
             const int inst = i * NW + w;               // wave-uniform
-            const int q = inst * 64 + lane;            // chunk index inside the tile
-            const int kk = q / ROW_CHUNKS;
-            const int pos = q % ROW_CHUNKS;
-            const int c = pos ^ layout::kswz(kk);
-            const int key = min(tile * KT + kk, T - 1);   // past T: any valid row, masked later
-            copy16_to_lds_off(Kbh, (uint32_t)(key * D + c * 8) * 2u, ks_lds + inst * 64 * 8);
-            copy16_to_lds_off(Vtile, (uint32_t)q * 16u, vs_lds + inst * 64 * 8);
+            copy16_to_lds_off(src + inst * 64 * 8, (uint32_t)lane * 16u, dst + inst * 64 * 8);
         }
     };
 
-    f32x4 o[MT_O][NT];
+    f32x16 o[MT_O][NR];
 #pragma unroll
     for (int mt = 0; mt < MT_O; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) o[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run[NT], l_run[NT];
+        for (int nt = 0; nt < NR; ++nt) o[mt][nt] = f32x16{};
+    float m_run[NR], l_run[NR];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) { m_run[nt] = -INFINITY; l_run[nt] = 0.f; }
+    for (int nt = 0; nt < NR; ++nt) { m_run[nt] = -INFINITY; l_run[nt] = 0.f; }
+
+    // LDS read offsets (elements) that depend only on the lane
+    const int krow = layout::swap23(n);                 // key row of the S^T A operand
+    const int k_off = krow * D;
+    const int k_swz = layout::swz32(krow, ROW_CHUNKS);
 
     issue(0, 0);
     for (int it = 0; it < n_tiles; ++it) {
@@ -173,133 +182,136 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
         wait_vmcnt<0>();            // this wave's copies of tile `it` have landed
         __syncthreads();            // ... and everyone's; all waves are done with tile it-1
         if (it + 1 < n_tiles) issue(it + 1, stage ^ 1);
-        bf16* ks_lds = smem + stage * 2 * TILE;
+        const bf16* ks_lds = smem + stage * 2 * TILE;
         const bf16* vs_lds = ks_lds + TILE;
 
-        // ---- S^T = K Q^T (this wave's head dims) --------------------------
-        f32x4 s[MT_S][NT];
+        // ---- S^T = K Q^T ---------------------------------------------------
+        // Two independent accumulator chains (even / odd contraction steps)
+        // and operand reads issued PF steps ahead of their MFMA.
+        constexpr int PF = 4;
+        f32x16 s[NR], s2[NR];
 #pragma unroll
-        for (int mt = 0; mt < MT_S; ++mt)
+        for (int nt = 0; nt < NR; ++nt) { s[nt] = f32x16{}; s2[nt] = f32x16{}; }
+        bf16x8 abuf[PF];
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) s[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks < PF; ++ks)
+            abuf[ks] = *(const bf16x8*)(ks_lds + k_off + (((2 * ks + h2) ^ k_swz) * 8));
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 a = abuf[ks % PF];
+            if (ks + PF < KS)
+                abuf[ks % PF] = *(const bf16x8*)(ks_lds + k_off + (((2 * (ks + PF) + h2) ^ k_swz) * 8));
 #pragma unroll
-            for (int mt = 0; mt < MT_S; ++mt) {
-                const int kk = layout::st_row_key(mt, n);
-                const int pos = (dbase / 8 + 4 * ks + g) ^ layout::kswz(kk);
-                const bf16x8 a = *(const bf16x8*)(ks_lds + kk * D + pos * 8);
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) s[mt][nt] = mfma_16x16x32(a, qb[nt][ks], s[mt][nt]);
+            for (int nt = 0; nt < NR; ++nt) {
+                if (ks & 1) s2[nt] = mfma_32x32x16(a, qb[nt][ks], s2[nt]);
+                else s[nt] = mfma_32x32x16(a, qb[nt][ks], s[nt]);
             }
         }
-        if constexpr (SPLIT == 2) {
-            // Sum the two halves of the contraction: every wave parks its
-            // partial scores in the (now idle) K tile and adds its partner's.
-            f32x4* xs = (f32x4*)ks_lds;
-            __syncthreads();
 #pragma unroll
-            for (int mt = 0; mt < MT_S; ++mt)
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) xs[(w * NSX + mt * NT + nt) * 64 + lane] = s[mt][nt];
-            __syncthreads();
-            const int pw = w ^ 1;
-#pragma unroll
-            for (int mt = 0; mt < MT_S; ++mt)
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const f32x4 other = xs[(pw * NSX + mt * NT + nt) * 64 + lane];
-                    // fixed summation order (lower head dims first) in both waves
-                    s[mt][nt] = hd == 0 ? s[mt][nt] + other : other + s[mt][nt];
-                }
-        }
+        for (int nt = 0; nt < NR; ++nt) s[nt] += s2[nt];
 
         // ---- mask + online softmax ----------------------------------------
         const int j0 = it * KT;
-        float mx[NT];
+        const bool edge = CAUSAL ? (j0 + KT - 1 > wave_tok_min) : (j0 + KT > T);
+        float mx[NR];
         bool need = false;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
+        for (int nt = 0; nt < NR; ++nt) {
             float mloc = -INFINITY;
 #pragma unroll
-            for (int mt = 0; mt < MT_S; ++mt) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int key = j0 + layout::st_c_key(mt, g, i);
+            for (int i = 0; i < 16; ++i) {
+                float v = s[nt][i] * scale_log2;
+                if (edge) {
+                    const int key = j0 + layout::c32_index(h2, i);
                     const bool vis = CAUSAL ? (key <= row_tok[nt]) : (key < T);
-                    const float v = vis ? s[mt][nt][i] * scale_log2 : -INFINITY;
-                    s[mt][nt][i] = v;
-                    mloc = fmaxf(mloc, v);
+                    v = vis ? v : -INFINITY;
                 }
+                s[nt][i] = v;
+                mloc = fmaxf(mloc, v);
             }
-            mx[nt] = max_over_groups(mloc);
+            mx[nt] = max_over_halves(mloc);
             need |= mx[nt] > m_run[nt] + kRescaleSlack;
         }
         if (__any(need)) {
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
+            for (int nt = 0; nt < NR; ++nt) {
                 const float mnew = fmaxf(m_run[nt], mx[nt]);
                 const float alpha = (m_run[nt] == -INFINITY) ? 0.f : fast_exp2(m_run[nt] - mnew);
                 m_run[nt] = mnew;
                 l_run[nt] *= alpha;
 #pragma unroll
-                for (int mt = 0; mt < MT_O; ++mt) o[mt][nt] *= alpha;
+                for (int mt = 0; mt < MT_O; ++mt) scale_acc(o[mt][nt], alpha);
             }
         }
-        bf16x8 pb[NT][KS_P];
+        bf16x8 pb[NR][KSP];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
+        for (int nt = 0; nt < NR; ++nt) {
             float lsum = 0.f;
 #pragma unroll
-            for (int mt = 0; mt < MT_S; ++mt) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float p = fast_exp2(s[mt][nt][i] - m_run[nt]);
-                    s[mt][nt][i] = p;
-                    lsum += p;
-                }
+            for (int i = 0; i < 16; ++i) {
+                const float p = fast_exp2(s[nt][i] - m_run[nt]);
+                s[nt][i] = p;
+                lsum += p;
             }
             l_run[nt] += lsum;
 #pragma unroll
-            for (int kp = 0; kp < KS_P; ++kp) pb[nt][kp] = pack_bf16x8(s[2 * kp][nt], s[2 * kp + 1][nt]);
+            for (int kp = 0; kp < KSP; ++kp) {
+                f32x4 lo = {s[nt][8 * kp + 0], s[nt][8 * kp + 1], s[nt][8 * kp + 2], s[nt][8 * kp + 3]};
+                f32x4 hi = {s[nt][8 * kp + 4], s[nt][8 * kp + 5], s[nt][8 * kp + 6], s[nt][8 * kp + 7]};
+                pb[nt][kp] = pack_bf16x8(lo, hi);
+            }
         }
 
-        // ---- O^T += V^T P^T (this wave's head dims) ---------------------------
+        // ---- O^T += V^T P^T --------------------------------------------------
+        // contraction step outer, head-dim tile inner: consecutive MFMAs go to
+        // different accumulators; V^T operand reads run PF steps ahead.
+        {
+            constexpr int NSTEP = KSP * MT_O;
+            bf16x8 vbuf[PF];
+            auto vaddr = [&](int step) {
+                const int kp = step / MT_O, mt = step % MT_O;
+                const int d = 32 * mt + krow;
+                return vs_lds + (d * RL + ((2 * kp + h2) ^ layout::swz32(d, RL))) * 8;
+            };
 #pragma unroll
-        for (int kp = 0; kp < KS_P; ++kp) {
+            for (int st = 0; st < PF; ++st) vbuf[st] = *(const bf16x8*)vaddr(st);
 #pragma unroll
-            for (int mt = 0; mt < MT_O; ++mt) {
-                const int d = dbase + layout::pv_row_d(mt, n);
-                const int pos = (4 * kp + g) ^ layout::vswz(d, RL);
-                const bf16x8 a = *(const bf16x8*)(vs_lds + (d * RL + pos) * 8);
+            for (int st = 0; st < NSTEP; ++st) {
+                const bf16x8 a = vbuf[st % PF];
+                if (st + PF < NSTEP) vbuf[st % PF] = *(const bf16x8*)vaddr(st + PF);
+                const int kp = st / MT_O, mt = st % MT_O;
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) o[mt][nt] = mfma_16x16x32(a, pb[nt][kp], o[mt][nt]);
+                for (int nt = 0; nt < NR; ++nt) o[mt][nt] = mfma_32x32x16(a, pb[nt][kp], o[mt][nt]);
             }
         }
     }
 
     // ---- epilogue: normalise, store ------------------------------------------
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        const float l = sum_over_groups(l_run[nt]);
+    for (int nt = 0; nt < NR; ++nt) {
+        const float l = sum_over_halves(l_run[nt]);
         const float inv = 1.f / l;
         if (!row_ok[nt]) continue;
         const size_t row = ((size_t)b * Hq + row_head[nt]) * T + row_tok[nt];
 #pragma unroll
-        for (int bq = 0; bq < DS / 32; ++bq) {
-            const f32x4 lo = o[2 * bq][nt] * inv;
-            const f32x4 hi = o[2 * bq + 1][nt] * inv;
-            const int d0 = dbase + 32 * bq + 8 * g;     // = dbase + pv_c_d(2bq, g, 0)
-            if constexpr (OUT_F32) {
-                float* dst = (float*)Out + row * D + d0;
-                *(f32x4*)dst = lo;
-                *(f32x4*)(dst + 4) = hi;
-            } else {
-                bf16* dst = (bf16*)Out + row * D + d0;
-                *(bf16x8*)dst = pack_bf16x8(lo, hi);
+        for (int mt = 0; mt < MT_O; ++mt) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const f32x16& acc = o[mt][nt];
+                const f32x4 lo = f32x4{acc[8 * half + 0], acc[8 * half + 1], acc[8 * half + 2], acc[8 * half + 3]} * inv;
+                const f32x4 hi = f32x4{acc[8 * half + 4], acc[8 * half + 5], acc[8 * half + 6], acc[8 * half + 7]} * inv;
+                const int d0 = 32 * mt + layout::c32_index(h2, 8 * half);
+                if constexpr (OUT_F32) {
+                    float* dst = (float*)Out + row * D + d0;
+                    *(f32x4*)dst = lo;
+                    *(f32x4*)(dst + 4) = hi;
+                } else {
+                    bf16* dst = (bf16*)Out + row * D + d0;
+                    *(bf16x8*)dst = pack_bf16x8(lo, hi);
+                }
             }
         }
-        if (Lse != nullptr && g == 0 && hd == 0) Lse[row] = m_run[nt] * kLn2 + __logf(l);
+        if (Lse != nullptr && h2 == 0) Lse[row] = m_run[nt] * kLn2 + __logf(l);
     }
 }
 
@@ -381,21 +393,21 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(const float* __restric
 // ---------------------------------------------------------------------------
 // Host-side launchers (validated arguments only).
 // ---------------------------------------------------------------------------
-template <int D, int NT, int NW, int KT, int SPLIT>
+template <int D, int NR, int NW, int KT>
 static hipError_t launch_bf16(const PrefillArgs& a) {
-    const int R = (NW / SPLIT) * 16 * NT;
+    const int R = NW * 32 * NR;
     const int tok = R / a.G;
     const int n_tok_blocks = (a.T + tok - 1) / tok;
     const int n_kv_tiles = (a.T + KT - 1) / KT;
-    bf16* vt = (bf16*)a.workspace;
-    hipLaunchKernelGGL((vt_pack_kernel<D, KT>), dim3(n_kv_tiles, a.B * a.Hkv), dim3(256), 0, a.stream,
-                       (const bf16*)a.v, vt, a.T, n_kv_tiles);
+    bf16* kvt = (bf16*)a.workspace;
+    hipLaunchKernelGGL((kv_pack_kernel<D, KT>), dim3(n_kv_tiles, a.B * a.Hkv), dim3(256), 0, a.stream,
+                       (const bf16*)a.k, (const bf16*)a.v, kvt, a.T, n_kv_tiles);
     const dim3 grid(n_tok_blocks, a.Hkv, a.B);
     const float sl2 = a.scale * kLog2e;
 #define MQA_PREFILL_LAUNCH(C, F)                                                                      \
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, NT, NW, KT, SPLIT, C, F>), grid, dim3(NW * 64), 0, a.stream, \
-                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)vt, a.out, a.lse, a.Hq, a.Hkv, a.T, \
-                       a.G, tok, n_tok_blocks, n_kv_tiles, sl2)
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, NR, NW, KT, C, F>), grid, dim3(NW * 64), 0, a.stream, \
+                       (const bf16*)a.q, (const bf16*)kvt, a.out, a.lse, a.Hq, a.Hkv, a.T, a.G, tok,      \
+                       n_tok_blocks, n_kv_tiles, sl2)
     if (a.causal) {
         if (a.out_f32) MQA_PREFILL_LAUNCH(true, true); else MQA_PREFILL_LAUNCH(true, false);
     } else {
@@ -422,8 +434,8 @@ static hipError_t launch_f32(const PrefillArgs& a) {
 PrefillPlan prefill_plan(int head_dim, int in_bf16) {
     PrefillPlan p{};
     if (!in_bf16) { p.rows_per_wg = 1 << 30; p.kt = 0; return p; }
-    if (head_dim == 512) { p.rows_per_wg = (8 / 2) * 16 * 2; p.kt = 32; }
-    else if (head_dim == 128) { p.rows_per_wg = 4 * 16 * 2; p.kt = 32; }
+    if (head_dim == 512) { p.rows_per_wg = 4 * 32 * 1; p.kt = 32; }
+    else if (head_dim == 128) { p.rows_per_wg = 4 * 32 * 2; p.kt = 32; }
     return p;
 }
 
@@ -441,8 +453,8 @@ hipError_t prefill_launch(const PrefillArgs& a) {
             default: return hipErrorInvalidValue;
         }
     }
-    if (a.D == 512) return launch_bf16<512, 2, 8, 32, 2>(a);
-    if (a.D == 128) return launch_bf16<128, 2, 4, 32, 1>(a);
+    if (a.D == 512) return launch_bf16<512, 1, 4, 32>(a);
+    if (a.D == 128) return launch_bf16<128, 2, 4, 32>(a);
     return hipErrorInvalidValue;
 }
 

@@ -88,9 +88,10 @@ const char* mqa_last_hip_error_name(void);
  *     size G = Hq/Hkv a power of two with G <= 128 (D=512) or G <= 256
  *     (D=128);
  *   in_dtype F32 -> out_dtype F32, D a multiple of 64 up to 512, any G.
- * Workspace: bf16 inputs need `mqa_prefill_workspace_size()` bytes (a tiled,
- * transposed copy of V that the library writes first); F32 needs none
- * (workspace may be NULL with workspace_bytes 0).
+ * Workspace: bf16 inputs need `mqa_prefill_workspace_size()` bytes, where the
+ * library first writes K and a transposed V as one stream of 32-key tiles
+ * (2 * B * Hkv * ceil(T/32) * 32 * D * 2 bytes); F32 needs none (workspace
+ * may be NULL with workspace_bytes 0).
  */
 size_t mqa_prefill_workspace_size(int B, int Hq, int Hkv, int T, int head_dim,
                                   int in_dtype);

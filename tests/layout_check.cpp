@@ -78,6 +78,45 @@ int main() {
         for (int g = 0; g < 4; ++g)
             for (int j = 0; j < 8; ++j)
                 if (pv_c_d(2 * b + (j >> 2), g, j & 3) != 32 * b + 8 * g + j) return fail("out cols", b, g);
+    // 5. 32x32x16 maps: accumulator (h, i) is row 8(i/4)+4h+i%4 of the A operand,
+    //    i.e. key swap23(row); the two lane halves cover each 16-key step.
+    for (int h = 0; h < 2; ++h)
+        for (int i = 0; i < 16; ++i)
+            if (c32_index(h, i) != swap23(8 * (i / 4) + 4 * h + (i % 4))) return fail("c32", h, i);
+    for (int ks = 0; ks < 2; ++ks) {
+        std::set<int> keys;
+        for (int h = 0; h < 2; ++h)
+            for (int j = 0; j < 8; ++j) keys.insert(c32_index(h, 8 * ks + j));
+        if ((int)keys.size() != 16 || *keys.begin() != 16 * ks) return fail("c32 kstep", ks, 0);
+    }
+    // 6. 32-row operand reads: 8-lane groups hit 8 distinct slots of 128 B and
+    //    16-lane groups 16 distinct slots of 256 B.
+    auto grp_ok = [](auto addr) {
+        for (int grp : {8, 16}) {
+            for (int base = 0; base < 64; base += grp) {
+                std::set<long> s;
+                for (int l = base; l < base + grp; ++l) s.insert((addr(l) / 16) % grp);
+                if ((int)s.size() != grp) return false;
+            }
+        }
+        return true;
+    };
+    for (int rc : {4, 8, 16, 64}) {
+        for (int blk = 0; blk < 16; ++blk)
+            for (int ks = 0; ks < rc / 2; ++ks) {
+                auto addr = [&](int l) {
+                    int r = 32 * blk + swap23(l % 32);
+                    int c = 2 * ks + l / 32;
+                    return ((long)r * rc + (c ^ swz32(r, rc))) * 16;
+                };
+                if (!grp_ok(addr)) return fail("32-row reads", rc, ks);
+            }
+        for (int r = 0; r < 512; ++r) {
+            std::set<int> s;
+            for (int c = 0; c < rc; ++c) s.insert(c ^ swz32(r, rc));
+            if ((int)s.size() != rc || *s.rbegin() != rc - 1) return fail("swz32 bijection", rc, r);
+        }
+    }
     std::printf("ok\n");
     return 0;
 }

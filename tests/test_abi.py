@@ -73,9 +73,9 @@ def test_prefill_empty_calls_are_ok():
 
 
 def test_prefill_workspace_size():
-    # bf16: a tiled transposed copy of V padded to whole 32-key tiles
-    assert lib.mqa_prefill_workspace_size(2, 16, 1, 4096, 512, BF16) == 2 * 1 * 4096 * 512 * 2
-    assert lib.mqa_prefill_workspace_size(1, 8, 2, 33, 128, BF16) == 1 * 2 * 64 * 128 * 2
+    # bf16: K and a transposed V as whole 32-key tiles
+    assert lib.mqa_prefill_workspace_size(2, 16, 1, 4096, 512, BF16) == 2 * 2 * 1 * 4096 * 512 * 2
+    assert lib.mqa_prefill_workspace_size(1, 8, 2, 33, 128, BF16) == 2 * 1 * 2 * 64 * 128 * 2
     assert lib.mqa_prefill_workspace_size(1, 16, 1, 128, 512, F32) == 0
 
 
