@@ -98,8 +98,16 @@ constexpr uint32_t kSelHiHalves = 0x07060302u;  // {lo.h1, hi.h1}
 
 // Max / sum over the two lane halves l, l^32 (the two halves holding one
 // output column of a 32x32 MFMA tile).
-__device__ __forceinline__ float max_over_halves(float v) { return fmaxf(v, __shfl_xor(v, 32)); }
-__device__ __forceinline__ float sum_over_halves(float v) { return v + __shfl_xor(v, 32); }
+// v_permlane32_swap with both operands = v leaves, in every lane, v of that
+// lane and of its partner l ^ 32 in the two results (no LDS round trip).
+__device__ __forceinline__ float max_over_halves(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_over_halves(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Max / sum over the four lanes l, l^16, l^32, l^48 (the four lane groups
 // that share one MFMA output column).
@@ -130,11 +138,71 @@ __device__ __forceinline__ void copy16_to_lds_off(const void* base, uint32_t byt
     __builtin_amdgcn_global_load_lds((const char*)base + byte_off, (lds_void*)lds_base_wave, 16, 0, 0);
 }
 
+// The same 16-byte global->LDS copy issued from inline asm: base (wave-
+// uniform, SGPR pair) + voff (per lane) -> LDS byte address lds_byte + 16*lane.
+// Used inside loops that also read LDS: when the compiler sees an LDS DMA in
+// flight it stops tracking LDS reads precisely and waits for all of them
+// (lgkmcnt(0)) before every use.  The asm has no register outputs; callers
+// wait with wait_vmcnt<0>() and a barrier before reading the destination.
+// The leading s_nop covers a VALU->SGPR->VMEM read hazard on the base.
+__device__ __forceinline__ void copy16_to_lds_async(const void* base, uint32_t voff, uint32_t lds_byte) {
+    asm volatile(
+        "s_nop 4\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %0, %1"
+        :
+        : "v"(voff), "s"(base), "s"(lds_byte)
+        : "memory", "m0");
+}
+
+// Same, with up to VALU vector-ALU instructions (transcendentals included)
+// placed after each MFMA: lets independent softmax work fill the MFMA
+// shadow of a single wave.
+template <int FIRST, int STEPS, int VALU>
+__device__ __forceinline__ void sched_reads_ahead_valu() {
+    __builtin_amdgcn_sched_group_barrier(0x100, FIRST, 0);
+#pragma unroll
+    for (int i = 0; i < STEPS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, VALU, 0);
+    }
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+
+// s_waitcnt vmcnt(n) for a wave-uniform n known to be one of {0, A, B, A+B}.
+template <int A, int B>
+__device__ __forceinline__ void wait_vmcnt_of(int n) {
+    if (n == A + B) wait_vmcnt<A + B>();
+    else if (n == B) wait_vmcnt<B>();
+    else if (n == A) wait_vmcnt<A>();
+    else wait_vmcnt<0>();
+}
+
+// 32-bit LDS byte address of a __shared__ object
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(const T* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(const char*)p;
+}
+
+// Scheduling hints: ask the compiler to place `first` LDS reads, then
+// alternate one MFMA with one LDS read `steps` times (keeps reads running
+// `first` operands ahead of the MFMA that consumes them).
+template <int FIRST, int STEPS>
+__device__ __forceinline__ void sched_reads_ahead() {
+    __builtin_amdgcn_sched_group_barrier(0x100, FIRST, 0);
+#pragma unroll
+    for (int i = 0; i < STEPS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+}
+
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }

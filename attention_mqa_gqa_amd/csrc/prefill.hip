@@ -17,6 +17,8 @@
 //     diagonal tile is masked per element, and the heaviest blocks start
 //     first.
 // fp32 path: a plain fp32 VALU kernel (no reduced-precision operands).
+#include <type_traits>
+
 #include "common.hpp"
 #include "layout.hpp"
 #include "kernels.hpp"
@@ -25,9 +27,11 @@ namespace mqa {
 
 // ---------------------------------------------------------------------------
 // K, V [B*Hkv, T, D] -> tile stream [B*Hkv, n_tiles, (K tile | V^T tile)].
-// Each 32-key tile is stored exactly as the prefill kernel keeps it in LDS:
-// the K tile row-major (row = key) and the V^T tile (row = head dim, 32 keys
-// per row), both with 16-byte chunks in swizzled order, zero past T.  V's
+// Each 32-key tile is stored as the prefill kernel keeps it in LDS: the K
+// tile row-major (row = key; 16-byte chunks in swizzled order unless a row
+// is exactly one 1 KB copy, which the kernel places with padding instead)
+// and the V^T tile (row = head dim, 32 keys per row, swizzled chunks), zero
+// past T.  V's
 // contraction index (the key) is its row index, so the P.V operand needs it
 // transposed; doing that here once, and storing both tiles contiguously,
 // turns every global->LDS copy of the main kernel into a straight 16-byte
@@ -47,10 +51,11 @@ __global__ __launch_bounds__(256) void kv_pack_kernel(const bf16* __restrict__ K
     bf16* kdst = KVt + (bh * n_tiles + tile) * (size_t)(2 * TILE);
     bf16* vdst = kdst + TILE;
     // K tile: chunk position p of row kk holds global chunk p ^ swz(kk)
+    // (plain order for 1 KB rows)
     for (int q = threadIdx.x; q < KT * ROW_CHUNKS; q += 256) {
         const int kk = q / ROW_CHUNKS;
         const int p = q % ROW_CHUNKS;
-        const int c = p ^ layout::swz32(kk, ROW_CHUNKS);
+        const int c = (2 * D == 1024) ? p : (p ^ layout::swz32(kk, ROW_CHUNKS));
         const int key = tile * KT + kk;
         const u32x4 val = key < T ? ldg16(ksrc + (size_t)key * D + c * 8) : u32x4{0, 0, 0, 0};
         *(u32x4*)(kdst + (size_t)q * 8) = val;
@@ -103,12 +108,21 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     constexpr int KSP = KT / 16;          // P.V contraction steps
     constexpr int RL = KT / 8;            // chunks per V^T row
     constexpr int TILE = KT * D;          // elements per K tile (and per V^T tile)
-    constexpr int LOADS = 2 * TILE / 8 / (NW * 64);   // 16-byte copies per thread per tile
+    constexpr int LH = TILE / 8 / (NW * 64);   // 16-byte copies per thread per K (or V^T) tile
     constexpr int ROW_CHUNKS = D / 8;
+    // K rows of 1 KB (D = 512) are one copy instruction each, so in LDS each
+    // row can start 16 bytes after the previous one ends: rows then fall on
+    // distinct bank slots without any swizzle, and a lane reads every
+    // contraction step of its row from one address register plus an
+    // immediate offset.  Narrower rows are swizzled instead.
+    constexpr bool KPAD = (2 * D == 1024);
+    constexpr int KROW_B = KPAD ? 2 * D + 16 : 2 * D;     // LDS bytes per K row
+    constexpr int KSTAGE_B = KT * KROW_B;                  // LDS bytes per K stage
+    constexpr int VSTAGE_B = 2 * TILE;                     // LDS bytes per V^T stage
     static_assert(KT == 32, "key tile");
-    static_assert((2 * TILE / 8) % (NW * 64) == 0, "tile must split evenly over the waves");
+    static_assert((TILE / 8) % (NW * 64) == 0, "tile must split evenly over the waves");
 
-    __shared__ __attribute__((aligned(16))) bf16 smem[2 * 2 * TILE];
+    __shared__ __attribute__((aligned(16))) char smem[2 * KSTAGE_B + 2 * VSTAGE_B];
 
     const int lane = lane_id();
     const int w = wave_id();
@@ -130,7 +144,6 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
         row_head[nt] = hk * G + r % G;
         row_ok[nt] = (r < rows_used) && (row_tok[nt] < T);
     }
-    int wave_tok_min = t0 + (w * RW) / G;      // smallest token among this wave's rows
 
     // Q^T operands: lane half h2 holds head dims 16ks + 8h2 .. +7 of row n.
     bf16x8 qb[NR][KS];
@@ -151,14 +164,31 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     const int t_last = min(T, t0 + tok_per_wg) - 1;
     const int n_tiles = CAUSAL ? (t_last / KT + 1) : n_kv_tiles;
 
-    // tile `tile` of the packed stream -> LDS stage: a straight contiguous copy
-    auto issue = [&](int tile, int stage) {
+    // LDS: K stages 0/1, then V^T stages 0/1; tile j lives in stage j & 1.
+    // Iteration t computes S(t+1) next to softmax(t) (between barriers A and
+    // B), then P(t).V(t).  Right after barrier A it copies V(t+1) into the
+    // stage of V(t-1) (read by P(t-1).V(t-1), before A); right after barrier
+    // B it copies K(t+3) into the stage of K(t+1) (read by S(t+1), before B).
+    // Copies are issued in the order they are consumed, so in-order vmcnt
+    // waits are exact.
+    const uint32_t lds_base = lds_addr(smem);
+    const uint32_t lane16 = (uint32_t)lane * 16u;
+    auto issue_k = [&](int tile) {
         const bf16* src = KVbh + (size_t)tile * 2 * TILE;
-        bf16* dst = smem + stage * 2 * TILE;
+        const uint32_t dst = lds_base + (uint32_t)((tile & 1) * KSTAGE_B);
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
+        for (int i = 0; i < LH; ++i) {
             const int inst = i * NW + w;               // wave-uniform
-            copy16_to_lds_off(src + inst * 64 * 8, (uint32_t)lane * 16u, dst + inst * 64 * 8);
+            copy16_to_lds_async(src + inst * 64 * 8, lane16, dst + (uint32_t)inst * (KPAD ? KROW_B : 1024));
+        }
+    };
+    auto issue_v = [&](int tile) {
+        const bf16* src = KVbh + (size_t)tile * 2 * TILE + TILE;
+        const uint32_t dst = lds_base + (uint32_t)(2 * KSTAGE_B + (tile & 1) * VSTAGE_B);
+#pragma unroll
+        for (int i = 0; i < LH; ++i) {
+            const int inst = i * NW + w;
+            copy16_to_lds_async(src + inst * 64 * 8, lane16, dst + (uint32_t)inst * 1024u);
         }
     };
 
@@ -171,65 +201,108 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
 #pragma unroll
     for (int nt = 0; nt < NR; ++nt) { m_run[nt] = -INFINITY; l_run[nt] = 0.f; }
 
-    // LDS read offsets (elements) that depend only on the lane
-    const int krow = layout::swap23(n);                 // key row of the S^T A operand
-    const int k_off = krow * D;
-    const int k_swz = layout::swz32(krow, ROW_CHUNKS);
-
-    issue(0, 0);
-    for (int it = 0; it < n_tiles; ++it) {
-        const int stage = it & 1;
-        wait_vmcnt<0>();            // this wave's copies of tile `it` have landed
-        __syncthreads();            // ... and everyone's; all waves are done with tile it-1
-        if (it + 1 < n_tiles) issue(it + 1, stage ^ 1);
-        const bf16* ks_lds = smem + stage * 2 * TILE;
-        const bf16* vs_lds = ks_lds + TILE;
-
-        // ---- S^T = K Q^T ---------------------------------------------------
-        // Two independent accumulator chains (even / odd contraction steps)
-        // and operand reads issued PF steps ahead of their MFMA.
-        constexpr int PF = 4;
-        f32x16 s[NR], s2[NR];
+    // K operand of contraction step ks for this lane (key row swap23(n),
+    // head dims 16ks + 8h2 .. +7), as a byte offset into a K stage.  Padded
+    // rows: one base plus 32 ks.  Swizzled rows: the swizzle only permutes
+    // chunks within aligned groups of 16, so 8 lane offsets plus an
+    // immediate stride of 256 bytes per 8 steps cover every step.
+    const int krow = layout::swap23(n);
+    const uint32_t kpad_off = (uint32_t)(krow * KROW_B + h2 * 16);
+    uint32_t koff[KPAD ? 1 : 8];
+    if constexpr (!KPAD) {
+        const int k_swz = layout::swz32(krow, ROW_CHUNKS);
 #pragma unroll
-        for (int nt = 0; nt < NR; ++nt) { s[nt] = f32x16{}; s2[nt] = f32x16{}; }
+        for (int v = 0; v < 8; ++v) koff[v] = (uint32_t)(krow * 2 * D + (((2 * v + h2) ^ k_swz) * 16));
+    }
+    auto kread = [&](const char* kst, int ks) {
+        if constexpr (KPAD) return *(const bf16x8*)(kst + kpad_off + ks * 32);
+        else return *(const bf16x8*)(kst + koff[ks & 7] + (ks >> 3) * 256);
+    };
+    constexpr int PF = 4;
+
+    // full S^T of one tile into acc (prologue only)
+    auto s_all = [&](f32x16 (&acc)[NR], const char* kst) {
         bf16x8 abuf[PF];
 #pragma unroll
-        for (int ks = 0; ks < PF; ++ks)
-            abuf[ks] = *(const bf16x8*)(ks_lds + k_off + (((2 * ks + h2) ^ k_swz) * 8));
+        for (int j = 0; j < PF; ++j) abuf[j] = kread(kst, j);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const bf16x8 a = abuf[ks % PF];
-            if (ks + PF < KS)
-                abuf[ks % PF] = *(const bf16x8*)(ks_lds + k_off + (((2 * (ks + PF) + h2) ^ k_swz) * 8));
+            if (ks + PF < KS) abuf[ks % PF] = kread(kst, ks + PF);
+#pragma unroll
+            for (int nt = 0; nt < NR; ++nt) acc[nt] = mfma_32x32x16(a, qb[nt][ks], acc[nt]);
+        }
+    };
+
+    // prologue: copies K(0), K(1), V(0); S(0); then K(2) once every wave is
+    // done with K(0).  Global copy order: K0 K1 V0 K2 | V1 K3 | V2 K4 | ...
+    issue_k(0);
+    if (n_tiles > 1) issue_k(1);
+    issue_v(0);
+    wait_vmcnt_of<LH, LH>(n_tiles > 1 ? 2 * LH : LH);   // K(0) has landed
+    __syncthreads();
+    f32x16 s_cur[NR];
+#pragma unroll
+    for (int nt = 0; nt < NR; ++nt) s_cur[nt] = f32x16{};
+    s_all(s_cur, smem);
+    __syncthreads();
+    if (n_tiles > 2) issue_k(2);
+
+    for (int it = 0; it < n_tiles; ++it) {
+        const bool has_next = it + 1 < n_tiles;
+        const bool has_next2 = it + 2 < n_tiles;
+        // K(it+1) has landed; V(it) and K(it+2) may still be in flight
+        if (has_next) wait_vmcnt_of<LH, LH>(LH + (has_next2 ? LH : 0));
+        __syncthreads();                                       // barrier A
+        if (has_next) issue_v(it + 1);
+
+        f32x16 s_nxt[NR];
+#pragma unroll
+        for (int nt = 0; nt < NR; ++nt) s_nxt[nt] = f32x16{};
+        // S(it+1) is computed unconditionally so that it shares a basic block
+        // with the softmax of S(it) (on the last tile it reads a stale but
+        // valid K stage and is discarded).  The two are interleaved by hand:
+        // every step issues one S MFMA (operand read PF steps ahead) and the
+        // softmax work of one score element, so the VALU work fills the MFMA
+        // shadow of this wave.
+        const char* kst = smem + ((it + 1) & 1) * KSTAGE_B;
+        bf16x8 abuf[PF];
+#pragma unroll
+        for (int j = 0; j < PF; ++j) abuf[j] = kread(kst, j);
+        auto s_step = [&](int ks) {
+            const bf16x8 a = abuf[ks % PF];
+            if (ks + PF < KS) abuf[ks % PF] = kread(kst, ks + PF);
+#pragma unroll
+            for (int nt = 0; nt < NR; ++nt) s_nxt[nt] = mfma_32x32x16(a, qb[nt][ks], s_nxt[nt]);
+        };
+        static_assert(KS >= 32 || D == 128, "interleave expects 32 steps at D = 512");
+
+        // first half: scale, mask (branch-free) and row max of S(it)
+        const int j0 = it * KT;
+        int lim[NR];
+        float mloc[NR];
+#pragma unroll
+        for (int nt = 0; nt < NR; ++nt) {
+            lim[nt] = (CAUSAL ? min(row_tok[nt], T - 1) : T - 1) - j0;
+            mloc[nt] = -INFINITY;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (i < KS / 2) s_step(i);
 #pragma unroll
             for (int nt = 0; nt < NR; ++nt) {
-                if (ks & 1) s2[nt] = mfma_32x32x16(a, qb[nt][ks], s2[nt]);
-                else s[nt] = mfma_32x32x16(a, qb[nt][ks], s[nt]);
+                const float v = layout::c32_index(h2, i) <= lim[nt] ? s_cur[nt][i] * scale_log2 : -INFINITY;
+                s_cur[nt][i] = v;
+                mloc[nt] = fmaxf(mloc[nt], v);
             }
         }
 #pragma unroll
-        for (int nt = 0; nt < NR; ++nt) s[nt] += s2[nt];
-
-        // ---- mask + online softmax ----------------------------------------
-        const int j0 = it * KT;
-        const bool edge = CAUSAL ? (j0 + KT - 1 > wave_tok_min) : (j0 + KT > T);
+        for (int i = 16; i < KS / 2; ++i) s_step(i);
         float mx[NR];
         bool need = false;
 #pragma unroll
         for (int nt = 0; nt < NR; ++nt) {
-            float mloc = -INFINITY;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float v = s[nt][i] * scale_log2;
-                if (edge) {
-                    const int key = j0 + layout::c32_index(h2, i);
-                    const bool vis = CAUSAL ? (key <= row_tok[nt]) : (key < T);
-                    v = vis ? v : -INFINITY;
-                }
-                s[nt][i] = v;
-                mloc = fmaxf(mloc, v);
-            }
-            mx[nt] = max_over_halves(mloc);
+            mx[nt] = max_over_halves(mloc[nt]);
             need |= mx[nt] > m_run[nt] + kRescaleSlack;
         }
         if (__any(need)) {
@@ -243,35 +316,54 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
                 for (int mt = 0; mt < MT_O; ++mt) scale_acc(o[mt][nt], alpha);
             }
         }
+        // second half: exp, row sum, pack P(it)
+        float lsum[NR];
+#pragma unroll
+        for (int nt = 0; nt < NR; ++nt) lsum[nt] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (KS / 2 + i < KS) s_step(KS / 2 + i);
+#pragma unroll
+            for (int nt = 0; nt < NR; ++nt) {
+                const float p = fast_exp2(s_cur[nt][i] - m_run[nt]);
+                s_cur[nt][i] = p;
+                lsum[nt] += p;
+            }
+        }
+#pragma unroll
+        for (int i = KS / 2 + 16; i < KS; ++i) s_step(i);
+        // keep the score accumulator in VGPRs: the O^T accumulator fills
+        // the AGPRs at D = 512
+#pragma unroll
+        for (int nt = 0; nt < NR; ++nt) asm volatile("" : "+v"(s_nxt[nt]));
         bf16x8 pb[NR][KSP];
 #pragma unroll
         for (int nt = 0; nt < NR; ++nt) {
-            float lsum = 0.f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float p = fast_exp2(s[nt][i] - m_run[nt]);
-                s[nt][i] = p;
-                lsum += p;
-            }
-            l_run[nt] += lsum;
+            l_run[nt] += lsum[nt];
 #pragma unroll
             for (int kp = 0; kp < KSP; ++kp) {
-                f32x4 lo = {s[nt][8 * kp + 0], s[nt][8 * kp + 1], s[nt][8 * kp + 2], s[nt][8 * kp + 3]};
-                f32x4 hi = {s[nt][8 * kp + 4], s[nt][8 * kp + 5], s[nt][8 * kp + 6], s[nt][8 * kp + 7]};
+                f32x4 lo = {s_cur[nt][8 * kp + 0], s_cur[nt][8 * kp + 1], s_cur[nt][8 * kp + 2], s_cur[nt][8 * kp + 3]};
+                f32x4 hi = {s_cur[nt][8 * kp + 4], s_cur[nt][8 * kp + 5], s_cur[nt][8 * kp + 6], s_cur[nt][8 * kp + 7]};
                 pb[nt][kp] = pack_bf16x8(lo, hi);
             }
         }
 
+        // V(it) has landed (K(it+2) and V(it+1) may still be in flight)
+        wait_vmcnt_of<LH, LH>((has_next2 ? LH : 0) + (has_next ? LH : 0));
+        __syncthreads();                                       // barrier B
+        if (it + 3 < n_tiles) issue_k(it + 3);
+
         // ---- O^T += V^T P^T --------------------------------------------------
-        // contraction step outer, head-dim tile inner: consecutive MFMAs go to
-        // different accumulators; V^T operand reads run PF steps ahead.
+        // contraction step outer, head-dim tile inner; V^T operand reads run
+        // PF steps ahead.
         {
             constexpr int NSTEP = KSP * MT_O;
+            const char* vl = smem + 2 * KSTAGE_B + (it & 1) * VSTAGE_B;
             bf16x8 vbuf[PF];
             auto vaddr = [&](int step) {
                 const int kp = step / MT_O, mt = step % MT_O;
                 const int d = 32 * mt + krow;
-                return vs_lds + (d * RL + ((2 * kp + h2) ^ layout::swz32(d, RL))) * 8;
+                return vl + (d * RL + ((2 * kp + h2) ^ layout::swz32(d, RL))) * 16;
             };
 #pragma unroll
             for (int st = 0; st < PF; ++st) vbuf[st] = *(const bf16x8*)vaddr(st);
@@ -283,7 +375,10 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
 #pragma unroll
                 for (int nt = 0; nt < NR; ++nt) o[mt][nt] = mfma_32x32x16(a, pb[nt][kp], o[mt][nt]);
             }
+            if constexpr (NR == 1) sched_reads_ahead<PF, NSTEP - PF>();
         }
+#pragma unroll
+        for (int nt = 0; nt < NR; ++nt) s_cur[nt] = s_nxt[nt];
     }
 
     // ---- epilogue: normalise, store ------------------------------------------
