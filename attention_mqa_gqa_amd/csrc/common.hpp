@@ -122,6 +122,14 @@ __device__ __forceinline__ float sum_over_groups(float v) {
     return v;
 }
 
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane
+// 4s + a loads 4 bf16 (8 bytes); lane i receives element i % 4 of the load
+// of lane 4s + i / 4 in slot s.  With lanes 4s..4s+3 reading 16 consecutive
+// columns of row s of a row-major block, lane i gets column i of rows 0..3.
+__device__ __forceinline__ s16x4 lds_read_tr16(const void* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+}
+
 __device__ __forceinline__ u32x4 ldg16(const void* p) { return *(const u32x4*)p; }
 __device__ __forceinline__ bf16x8 ldg_bf16x8(const void* p) { return *(const bf16x8*)p; }
 

@@ -74,5 +74,24 @@ MQA_HD constexpr int swz32(int r, int row_chunks) {
     return row_chunks >= 16 ? swz32_16(r) : (row_chunks == 8 ? swz32_8(r) : swz32_4(r));
 }
 
+// Rows that are one 1 KB copy each (K rows at D = 512, MLA latent rows) are
+// stored with 16 bytes of padding, key row r at row position swap23(r): the
+// lane that reads key swap23(n) reads position n, and 8 (16) consecutive
+// lanes hit 8 (16) distinct bank slots without any swizzle.
+MQA_HD constexpr int padded_row_bytes(int row_bytes) { return row_bytes + 16; }
+MQA_HD constexpr int padded_row_pos(int key_row) { return swap23(key_row & 31) | (key_row & ~31); }
+
+// MLA-absorbed decode tiles (32 cache rows).
+// Latent rows (1 KB + 16 B padding): row k of the tile sits at row position
+// 8(k/8) + 2(k%4) + (k/4)%2.  Score reads (lane n reads row n) then hit
+// distinct bank slots over 8 and 16 lanes, and a transposing 64-bit read of
+// four consecutive rows (one 16-lane group) touches 4 x 32 distinct bytes
+// of every 128-byte bank window.
+MQA_HD constexpr int mla_lat_pos(int k) { return (k & ~7) | ((k & 3) << 1) | ((k >> 2) & 1); }
+// RoPE rows (128 B = 8 chunks): chunk c of row r at position c ^ mla_rope_swz(r).
+MQA_HD constexpr int mla_rope_swz(int r) { return (r ^ (r >> 3)) & 7; }
+// P tile (one 64-byte row of 32 keys per head): chunk c at c ^ ptile_swz(h).
+MQA_HD constexpr int ptile_swz(int h) { return ((h >> 1) ^ (h >> 2)) & 3; }
+
 }  // namespace layout
 }  // namespace mqa

@@ -8,14 +8,18 @@
 // 64-d RoPE key is the part that cannot be absorbed (makesence §4.5;
 // walkerchi "Full 路线" §四 4.2).  Each cached row is read from HBM once per
 // step and used by all heads:
-//   * one workgroup (8 waves) = one (sequence, chunk of rows), all heads;
-//     wave w owns heads 16w .. 16w+15;
+//   * one workgroup (4 waves, one per SIMD) = one (sequence, chunk of rows)
+//     and all (up to 128) heads;
 //   * 32-row tiles are copied global -> LDS with asynchronous direct-to-LDS
-//     loads (double buffered, swizzled); the latent part of each tile is then
-//     transposed once in LDS for the P.V operand;
-//   * S^T = KV q_abs^T (K = 576 = 18 steps of 32) and O^T += V^T P^T
-//     (V^T = first 512 columns) on v_mfma_f32_16x16x32_bf16, fp32
-//     accumulation, online softmax in registers;
+//     loads, three stages deep (two tiles in flight);
+//   * scores: wave w computes S^T = KV q_abs^T for heads 32w..32w+31 on
+//     v_mfma_f32_32x32x16_bf16 (36 contraction steps over the 576-wide
+//     row), then the online softmax of those heads;
+//   * P (bf16) of every head goes to LDS, and each wave accumulates
+//     O^T += V^T P^T for ITS quarter of the 512 value dims and all heads:
+//     every V^T operand then feeds four MFMAs, so LDS traffic per MFMA is a
+//     quarter of a full-width split.  V^T operands come straight from the
+//     row-major latent tile through transposing LDS reads;
 //   * partials per (head, split) are merged by the shared log-sum-exp kernel.
 #include "common.hpp"
 #include "layout.hpp"
@@ -24,29 +28,36 @@
 namespace mqa {
 
 namespace {
-constexpr int kDK = 576;   // key width: latent + RoPE part
-constexpr int kDC = 512;   // latent width (= value width)
-constexpr int kDR = 64;    // RoPE part
-constexpr int kKT = 32;    // rows per tile
-constexpr int kNW = 8;     // waves per workgroup
+constexpr int kDK = 576;    // key width: latent + RoPE part
+constexpr int kDC = 512;    // latent width (= value width)
+constexpr int kDR = 64;     // RoPE part
+constexpr int kKT = 32;     // cache rows per tile
+constexpr int kNW = 4;      // waves per workgroup
+constexpr int kHW = 32;     // heads per wave (scores and softmax)
+constexpr int kHMAX = kNW * kHW;                                 // 128
+constexpr int kDW = kDC / kNW;                                   // value dims per wave (128)
+constexpr int kNS = 3;                                           // tile stages
+constexpr int kLatRowB = layout::padded_row_bytes(2 * kDC);      // 1040
+constexpr int kLatB = kKT * kLatRowB;                            // 33280
+constexpr int kRopeB = kKT * kDR * 2;                            // 4096
+constexpr int kStageB = kLatB + kRopeB;                          // 37376
+constexpr int kPB = kHMAX * kKT * 2;                             // P tile: 8192
+constexpr int kLdsB = kNS * kStageB + 2 * kPB + 2 * kHMAX * 4;
 }  // namespace
 
-__global__ __launch_bounds__(kNW * 64, 1) void mla_split_kernel(
+__global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
     const bf16* __restrict__ Qa, const bf16* __restrict__ KV, const int32_t* __restrict__ seq_lens,
     float* __restrict__ part_o, float* __restrict__ part_ml, int H, int max_len, int chunk, int n_split,
     float scale_log2) {
-    constexpr int KS_LAT = kDC / 32;        // 16
-    constexpr int KS_ROPE = kDR / 32;       // 2
-    constexpr int KS = KS_LAT + KS_ROPE;    // 18
-    constexpr int MT_S = kKT / 16;          // 2
-    constexpr int MT_O = kDC / 16;          // 32
-    constexpr int LAT_TILE = kKT * kDC;     // elements
-    constexpr int ROPE_TILE = kKT * kDR;
-    constexpr int RL = kKT / 8;             // chunks per V^T row (4)
+    constexpr int KS = kDK / 16;         // 36 score steps
+    constexpr int KS_LAT = kDC / 16;     // 32 of them over the latent
+    constexpr int MT = kDW / 32;         // 4 O^T M-tiles (value dims) per wave
+    constexpr int NT = kHMAX / 32;       // 4 O^T N-tiles (heads)
+    constexpr int PF = 4;                // operand read-ahead
 
-    __shared__ __attribute__((aligned(16))) bf16 lat[2][LAT_TILE];
-    __shared__ __attribute__((aligned(16))) bf16 rope[2][ROPE_TILE];
-    __shared__ __attribute__((aligned(16))) bf16 vt[LAT_TILE];
+    __shared__ __attribute__((aligned(16))) char smem[kLdsB];
+    char* const pbuf = smem + kNS * kStageB;                    // [2][kPB]
+    float* const alpha_buf = (float*)(pbuf + 2 * kPB);          // [2][kHMAX]
 
     const int s_idx = blockIdx.x;
     const int b = blockIdx.y;
@@ -58,161 +69,222 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_split_kernel(
 
     const int lane = lane_id();
     const int w = wave_id();
-    const int g = lane >> 4;
-    const int n = lane & 15;
-    const int tid = threadIdx.x;
-    const bool active = 16 * w < H;
-    const int head = 16 * w + n;
+    const int h2 = lane >> 5;
+    const int n = lane & 31;
+    const int head = kHW * w + n;                // head whose scores this lane holds
+    const bool head_ok = head < H;
 
-    const bf16* KVb = KV + (size_t)b * max_len * kDK;
-
+    // q_abs^T operands: lane half h2 holds dims 16ks + 8h2 .. +7 of `head`
     bf16x8 qb[KS];
     {
-        const bf16* qrow = Qa + ((size_t)b * H + (active ? head : 0)) * kDK;
+        const bf16* qrow = Qa + ((size_t)b * H + (head_ok ? head : 0)) * kDK;
+        const u32x4 zero = {0, 0, 0, 0};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const int c = ks < KS_LAT ? 32 * ks + 8 * g : kDC + 32 * (ks - KS_LAT) + 8 * g;
-            qb[ks] = ldg_bf16x8(qrow + c);
+            const u32x4 v = ldg16(qrow + 16 * ks + 8 * h2);
+            qb[ks] = __builtin_bit_cast(bf16x8, head_ok ? v : zero);
         }
     }
 
-    // 36 one-KB copies per tile: 32 latent rows (one row each) + 4 for the RoPE block.
-    auto issue = [&](int tile, int stage) {
+    const bf16* KVb = KV + (size_t)b * max_len * kDK;
+    const uint32_t lds_base = lds_addr(smem);
+    const uint32_t lane16 = (uint32_t)lane * 16u;
+    // One tile = 32 latent rows (one 1 KB copy each, padded positions) + the
+    // 32 RoPE parts (4 copies, swizzled through the per-lane source offset):
+    // 9 copies per wave.  Rows past the chunk end re-read the last row and
+    // are masked.
+    constexpr int kCopiesPerWave = (kKT + kRopeB / 1024) / kNW;
+    static_assert(kCopiesPerWave * kNW == kKT + kRopeB / 1024, "copies must split evenly over the waves");
+    auto issue = [&](int tile) {
+        const uint32_t st = lds_base + (uint32_t)((tile % kNS) * kStageB);
+        const int row0 = begin + tile * kKT;
 #pragma unroll
-        for (int r = 0; r < 5; ++r) {
-            const int u = r * kNW + w;          // wave-uniform
-            if (u < 32) {
-                const int kk = u;
-                const int key = min(begin + tile * kKT + kk, end - 1);
-                const int c = lane ^ layout::kswz(kk);
-                copy16_to_lds_off(KVb + (size_t)key * kDK, (uint32_t)c * 16u, &lat[stage][kk * kDC]);
-            } else if (u < 36) {
-                const int q = (u - 32) * 64 + lane;
-                const int kk = q >> 3;
-                const int c = (q & 7) ^ layout::swz8(kk);
-                const int key = min(begin + tile * kKT + kk, end - 1);
-                copy16_to_lds_off(KVb, (uint32_t)(key * kDK + kDC + c * 8) * 2u, &rope[stage][(u - 32) * 512]);
-            }
+        for (int i = 0; i < kKT / kNW; ++i) {
+            const int u = i * kNW + w;               // wave-uniform latent row
+            const int key = min(row0 + u, end - 1);
+            copy16_to_lds_async(KVb + (size_t)key * kDK, lane16, st + (uint32_t)(layout::mla_lat_pos(u) * kLatRowB));
+        }
+        {
+            const int r = 8 * w + (lane >> 3);       // RoPE row of this lane
+            const int c = (lane & 7) ^ layout::mla_rope_swz(r);
+            const int key = min(row0 + r, end - 1);
+            copy16_to_lds_async(KVb, (uint32_t)key * (kDK * 2u) + (uint32_t)(kDC * 2 + c * 16), st + (uint32_t)(kLatB + w * 1024));
         }
     };
 
-    f32x4 o[MT_O];
+    // score operand offsets (bytes within a stage)
+    const uint32_t lat_off = (uint32_t)(layout::mla_lat_pos(n) * kLatRowB + h2 * 16);
+    uint32_t rope_off[KS - KS_LAT];
 #pragma unroll
-    for (int mt = 0; mt < MT_O; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < KS - KS_LAT; ++j)
+        rope_off[j] = (uint32_t)(kLatB + n * 128 + (((2 * j + h2) ^ layout::mla_rope_swz(n)) * 16));
+    auto kread = [&](const char* st, int ks) {
+        if (ks < KS_LAT) return *(const bf16x8*)(st + lat_off + ks * 32);
+        return *(const bf16x8*)(st + rope_off[ks - KS_LAT]);
+    };
+    // transposing V^T reads: 16-lane group q = lane / 16, lane j = 4s + a in
+    // it reads latent row 16kp + 8h2 + 4r + s, value dims 128w + 32mt +
+    // 16(q%2) + 4a .. +3; the result is the A operand for value dims
+    // 128w + 32mt + (lane % 32), keys 16kp + 8h2 .. +7 (r = 0, 1).
+    const int tj = lane & 15;
+    const uint32_t tr_off = (uint32_t)((8 * h2 + 2 * (tj >> 2)) * kLatRowB +
+                                       2 * (kDW * w + 16 * ((lane >> 4) & 1) + 4 * (tj & 3)));
+    auto vread = [&](const char* st, int kp, int mt) {
+        const char* p = st + tr_off + kp * 16 * kLatRowB + mt * 64;
+        const s16x4 lo = lds_read_tr16(p);
+        const s16x4 hi = lds_read_tr16(p + kLatRowB);
+        typedef short s16x8 __attribute__((ext_vector_type(8)));
+        const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return __builtin_bit_cast(bf16x8, v);
+    };
+
+    f32x16 o[MT][NT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) o[mt][nt] = f32x16{};
     float m_run = -INFINITY, l_run = 0.f;
 
-    issue(0, 0);
-    for (int it = 0; it < n_tiles; ++it) {
-        const int stage = it & 1;
-        wait_vmcnt<0>();
-        __syncthreads();
-        // transpose the latent tile: thread (kb, db) moves an 8x8 block, in
-        // two 4-row halves (each half gives 4 keys = 8 bytes per head dim)
-        if (tid < 256) {
-            const int kb = tid & 3;
-            const int db = tid >> 2;
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                u32x4 r[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int kk = 8 * kb + 4 * half + j;
-                    r[j] = *(const u32x4*)&lat[stage][kk * kDC + (db ^ layout::kswz(kk)) * 8];
-                }
-#pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    const int d = 8 * db + t;
-                    const uint32_t sel = (t & 1) ? kSelHiHalves : kSelLoHalves;
-                    const int wd = t >> 1;
-                    u32x2 ov;
-                    ov.x = perm(r[1][wd], r[0][wd], sel);
-                    ov.y = perm(r[3][wd], r[2][wd], sel);
-                    *(u32x2*)&vt[(d * RL + (kb ^ layout::swz4(d))) * 8 + 4 * half] = ov;
-                }
-            }
-        }
-        __syncthreads();
-        if (it + 1 < n_tiles) issue(it + 1, stage ^ 1);
-        if (!active) continue;
+    // Tile t lives in stage t % 3.  Iteration t: scores and softmax of t,
+    // P(t) and the per-head rescale factors to LDS, barrier, then copies of
+    // tile t+2 (into the stage of tile t-1, whose P.V every wave finished
+    // before the barrier) and P(t).V(t).  Tiles t+1 and t+2 are in flight
+    // meanwhile; each wave waits for its own copies of t+1 before the barrier.
+    issue(0);
+    if (n_tiles > 1) issue(1);
+    if (n_tiles > 1) wait_vmcnt<kCopiesPerWave>(); else wait_vmcnt<0>();
+    __syncthreads();
 
-        // ---- S^T = KV q^T ----------------------------------------------------
-        f32x4 s[MT_S];
+    for (int it = 0; it < n_tiles; ++it) {
+        const char* st = smem + (it % kNS) * kStageB;
+
+        // ---- S^T = KV q_abs^T ------------------------------------------------
+        f32x16 s = f32x16{};
+        {
+            bf16x8 abuf[PF];
 #pragma unroll
-        for (int mt = 0; mt < MT_S; ++mt) s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < PF; ++j) abuf[j] = kread(st, j);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-            for (int mt = 0; mt < MT_S; ++mt) {
-                const int kk = layout::st_row_key(mt, n);
-                bf16x8 a;
-                if (ks < KS_LAT) {
-                    const int pos = (4 * ks + g) ^ layout::kswz(kk);
-                    a = *(const bf16x8*)&lat[stage][kk * kDC + pos * 8];
-                } else {
-                    const int pos = (4 * (ks - KS_LAT) + g) ^ layout::swz8(kk);
-                    a = *(const bf16x8*)&rope[stage][kk * kDR + pos * 8];
-                }
-                s[mt] = mfma_16x16x32(a, qb[ks], s[mt]);
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 a = abuf[ks % PF];
+                if (ks + PF < KS) abuf[ks % PF] = kread(st, ks + PF);
+                s = mfma_32x32x16(a, qb[ks], s);
             }
         }
-        // ---- mask + online softmax ---------------------------------------------
-        const int j0 = begin + it * kKT;
+
+        // ---- online softmax of heads 32w + n (keys 8(i/4) + 4h2 + i%4) ---------
+        const int row0 = begin + it * kKT;
         float mloc = -INFINITY;
+        if (row0 + kKT > end) {
 #pragma unroll
-        for (int mt = 0; mt < MT_S; ++mt) {
+            for (int i = 0; i < 16; ++i) {
+                const int key = row0 + 8 * (i >> 2) + 4 * h2 + (i & 3);
+                s[i] = key < end ? s[i] * scale_log2 : -INFINITY;
+                mloc = fmaxf(mloc, s[i]);
+            }
+        } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = j0 + layout::st_c_key(mt, g, i);
-                const float v = key < end ? s[mt][i] * scale_log2 : -INFINITY;
-                s[mt][i] = v;
-                mloc = fmaxf(mloc, v);
+            for (int i = 0; i < 16; ++i) {
+                s[i] *= scale_log2;
+                mloc = fmaxf(mloc, s[i]);
             }
         }
-        const float mx = max_over_groups(mloc);
-        if (__any(mx > m_run + kRescaleSlack)) {
+        const float mx = max_over_halves(mloc);
+        float alpha = 1.f;
+        if (mx > m_run + kRescaleSlack) {
             const float mnew = fmaxf(m_run, mx);
-            const float alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - mnew);
+            alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - mnew);
             m_run = mnew;
             l_run *= alpha;
-#pragma unroll
-            for (int mt = 0; mt < MT_O; ++mt) o[mt] *= alpha;
         }
+        float lsum = 0.f;
 #pragma unroll
-        for (int mt = 0; mt < MT_S; ++mt) {
+        for (int i = 0; i < 16; ++i) {
+            s[i] = fast_exp2(s[i] - m_run);
+            lsum += s[i];
+        }
+        l_run += lsum;
+        {
+            char* pl = pbuf + (it & 1) * kPB + head * 64 + 8 * h2;
+            const int sw = layout::ptile_swz(head);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float p = fast_exp2(s[mt][i] - m_run);
-                s[mt][i] = p;
-                l_run += p;
+            for (int c = 0; c < 4; ++c) {
+                u32x2 pk;
+                pk.x = pack_bf16x2(s[4 * c + 0], s[4 * c + 1]);
+                pk.y = pack_bf16x2(s[4 * c + 2], s[4 * c + 3]);
+                *(u32x2*)(pl + ((c ^ sw) * 16)) = pk;
             }
+            if (h2 == 0) alpha_buf[(it & 1) * kHMAX + head] = alpha;
         }
-        const bf16x8 pb = pack_bf16x8(s[0], s[1]);
-        // ---- O^T += V^T P^T -----------------------------------------------------
+
+        // tile it+1 has landed (nothing later was issued yet)
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (it + 2 < n_tiles) issue(it + 2);
+
+        // ---- O^T += V^T P^T for value dims 128w .. 128w+127, all heads ------------
+        {
+            const float* al = alpha_buf + (it & 1) * kHMAX;
+            float a4[NT];
+            bool need = false;
 #pragma unroll
-        for (int mt = 0; mt < MT_O; ++mt) {
-            const int d = layout::pv_row_d(mt, n);
-            const bf16x8 a = *(const bf16x8*)&vt[(d * RL + (g ^ layout::swz4(d))) * 8];
-            o[mt] = mfma_16x16x32(a, pb, o[mt]);
+            for (int nt = 0; nt < NT; ++nt) {
+                a4[nt] = al[32 * nt + n];
+                need |= a4[nt] != 1.f;
+            }
+            if (__any(need)) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) scale_acc(o[mt][nt], a4[nt]);
+            }
+            const char* pl = pbuf + (it & 1) * kPB;
+#pragma unroll
+            for (int kp = 0; kp < 2; ++kp) {
+                bf16x8 pb[NT];
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const int hh = 32 * nt + n;
+                    pb[nt] = *(const bf16x8*)(pl + hh * 64 + (((2 * kp + h2) ^ layout::ptile_swz(hh)) * 16));
+                }
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const bf16x8 va = vread(st, kp, mt);
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) o[mt][nt] = mfma_32x32x16(va, pb[nt], o[mt][nt]);
+                }
+            }
         }
     }
 
-    if (!active) return;
-    const float l_tot = sum_over_groups(l_run);
-    const size_t prow = ((size_t)b * H + head) * n_split + s_idx;
-#pragma unroll
-    for (int bq = 0; bq < kDC / 32; ++bq) {
-        float* dst = part_o + prow * kDC + 32 * bq + 8 * g;
-        *(f32x4*)dst = o[2 * bq];
-        *(f32x4*)(dst + 4) = o[2 * bq + 1];
+    // ---- partials: unnormalised O^T slices, (m, l) per head ---------------------
+    const float l_tot = sum_over_halves(l_run);
+    if (head_ok && h2 == 0) {
+        const size_t prow = ((size_t)b * H + head) * n_split + s_idx;
+        part_ml[2 * prow] = m_run;
+        part_ml[2 * prow + 1] = l_tot;
     }
-    if (g == 0) { part_ml[2 * prow] = m_run; part_ml[2 * prow + 1] = l_tot; }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int hh = 32 * nt + n;
+        if (hh >= H) continue;
+        float* dst = part_o + (((size_t)b * H + hh) * n_split + s_idx) * kDC + kDW * w + 4 * h2;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x16& acc = o[mt][nt];
+                *(f32x4*)(dst + 32 * mt + 8 * q) = f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+            }
+    }
 }
 
 DecodePlan mla_plan(int B, int max_len) {
+    // one workgroup per CU (LDS-bound): about 256 workgroups in total
     const int target_wgs = 256;
     int splits = (target_wgs + B - 1) / B;
     int chunk = (max_len + splits - 1) / splits;
-    if (chunk < 1024) chunk = 1024;
+    if (chunk < 512) chunk = 512;
     chunk = (chunk + kKT - 1) / kKT * kKT;
     DecodePlan p;
     p.chunk = chunk;
@@ -223,7 +295,7 @@ DecodePlan mla_plan(int B, int max_len) {
 
 hipError_t mla_launch(const MlaArgs& a) {
     const dim3 grid(a.plan.n_split, a.B);
-    hipLaunchKernelGGL(mla_split_kernel, grid, dim3(kNW * 64), 0, a.stream, (const bf16*)a.q, (const bf16*)a.kv,
+    hipLaunchKernelGGL(mla_decode_kernel, grid, dim3(kNW * 64), 0, a.stream, (const bf16*)a.q, (const bf16*)a.kv,
                        a.seq_lens, a.part_o, a.part_ml, a.H, a.max_len, a.plan.chunk, a.plan.n_split,
                        a.scale * kLog2e);
     hipError_t e = hipGetLastError();

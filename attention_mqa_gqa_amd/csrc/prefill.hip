@@ -111,12 +111,13 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     constexpr int LH = TILE / 8 / (NW * 64);   // 16-byte copies per thread per K (or V^T) tile
     constexpr int ROW_CHUNKS = D / 8;
     // K rows of 1 KB (D = 512) are one copy instruction each, so in LDS each
-    // row can start 16 bytes after the previous one ends: rows then fall on
+    // row can start 16 bytes after the previous one ends (and rows can be
+    // placed in any order): the 8 or 16 lanes served together then read
     // distinct bank slots without any swizzle, and a lane reads every
     // contraction step of its row from one address register plus an
     // immediate offset.  Narrower rows are swizzled instead.
     constexpr bool KPAD = (2 * D == 1024);
-    constexpr int KROW_B = KPAD ? 2 * D + 16 : 2 * D;     // LDS bytes per K row
+    constexpr int KROW_B = KPAD ? layout::padded_row_bytes(2 * D) : 2 * D;   // LDS bytes per K row
     constexpr int KSTAGE_B = KT * KROW_B;                  // LDS bytes per K stage
     constexpr int VSTAGE_B = 2 * TILE;                     // LDS bytes per V^T stage
     static_assert(KT == 32, "key tile");
@@ -179,7 +180,8 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
 #pragma unroll
         for (int i = 0; i < LH; ++i) {
             const int inst = i * NW + w;               // wave-uniform
-            copy16_to_lds_async(src + inst * 64 * 8, lane16, dst + (uint32_t)inst * (KPAD ? KROW_B : 1024));
+            const uint32_t pos = KPAD ? (uint32_t)layout::padded_row_pos(inst) * KROW_B : (uint32_t)inst * 1024u;
+            copy16_to_lds_async(src + inst * 64 * 8, lane16, dst + pos);
         }
     };
     auto issue_v = [&](int tile) {
@@ -207,7 +209,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     // chunks within aligned groups of 16, so 8 lane offsets plus an
     // immediate stride of 256 bytes per 8 steps cover every step.
     const int krow = layout::swap23(n);
-    const uint32_t kpad_off = (uint32_t)(krow * KROW_B + h2 * 16);
+    const uint32_t kpad_off = (uint32_t)(n * KROW_B + h2 * 16);
     uint32_t koff[KPAD ? 1 : 8];
     if constexpr (!KPAD) {
         const int k_swz = layout::swz32(krow, ROW_CHUNKS);
