@@ -34,13 +34,23 @@ COMMON_FLAGS = [
 ]
 
 
+# Kernels whose large O^T accumulators are pinned to AGPRs by inline asm
+# take the VGPR form for every compiler-generated MFMA, which keeps their
+# score accumulators in VGPRs (where the softmax reads them) instead of
+# shuffling one O^T tile between the two register files every key tile.
+PER_FILE_FLAGS = {
+    "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "mla_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def _sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src, extra):
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON_FLAGS, *extra, "-c", src, "-o", obj]
+    cmd = [HIPCC, *COMMON_FLAGS, *PER_FILE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(l for l in res.stderr.splitlines()
                      if "packed-fp32-ops" not in l and "not a recognized feature" not in l)

@@ -73,7 +73,7 @@ int mqa_prefill(const void* q, const void* k, const void* v, void* out, float* l
                 size_t workspace_bytes, void* stream) {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || T < 0 || head_dim <= 0) return MQA_ERR_INVALID_ARG;
     if (Hq % Hkv != 0) return MQA_ERR_INVALID_ARG;
-    if (!std::isfinite(scale)) return MQA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return MQA_ERR_INVALID_ARG;
     if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return MQA_ERR_INVALID_ARG;
     if (B == 0 || T == 0) return MQA_OK;
     if (!q || !k || !v || !out) return MQA_ERR_INVALID_ARG;
@@ -113,7 +113,7 @@ int mqa_decode(const void* q, const void* k_cache, const void* v_cache, const in
                void* workspace, size_t workspace_bytes, void* stream) {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || max_len < 0 || head_dim <= 0) return MQA_ERR_INVALID_ARG;
     if (Hq % Hkv != 0) return MQA_ERR_INVALID_ARG;
-    if (!std::isfinite(scale)) return MQA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return MQA_ERR_INVALID_ARG;
     if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return MQA_ERR_INVALID_ARG;
     if (B == 0) return MQA_OK;
     if (!q || !k_cache || !v_cache || !seq_lens || !out) return MQA_ERR_INVALID_ARG;
@@ -149,7 +149,7 @@ int mla_decode_absorbed(const void* q_abs, const void* kv_cache, const int32_t* 
                         int B, int H, int max_len, float scale, int dtype, int out_dtype, void* workspace,
                         size_t workspace_bytes, void* stream) {
     if (B < 0 || H <= 0 || max_len < 0) return MQA_ERR_INVALID_ARG;
-    if (!std::isfinite(scale)) return MQA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return MQA_ERR_INVALID_ARG;
     if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return MQA_ERR_INVALID_ARG;
     if (B == 0) return MQA_OK;
     if (!q_abs || !kv_cache || !seq_lens || !out) return MQA_ERR_INVALID_ARG;

@@ -44,6 +44,19 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(const bf16x8& a, const bf16x8& b
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// The same MFMA with the accumulator pinned to AGPRs (srcC = dst = acc).
+// Used for the large O^T accumulators so that the register allocator keeps
+// them in AGPRs and the score accumulators in VGPRs.  The compiler does not
+// know this is an MFMA, so it inserts no wait states after it: every
+// accumulator is used again only several MFMAs later, and code that reads
+// the accumulators otherwise must first call mfma_acc_drain().
+__device__ __forceinline__ void mfma_32x32x16_acc(const bf16x8& a, const bf16x8& b, f32x16& acc) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// 24 wait states: more than any MFMA result needs before a VALU or
+// v_accvgpr_read may read it
+__device__ __forceinline__ void mfma_acc_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
 // acc *= alpha for an accumulator tile that lives in AGPRs, one register at
 // a time through a temporary VGPR.  Written out so that the rare rescale of
 // the output accumulators does not make the compiler move them into VGPRs.
@@ -72,9 +85,11 @@ __device__ __forceinline__ f32x4 mfma_16x16x4_f32(float a, float b, const f32x4&
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Round-to-nearest-even fp32 -> bf16 (v_cvt_pk_bf16_f32 on gfx950).
+// two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    bf16 a = (bf16)lo, b = (bf16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
 
 __device__ __forceinline__ bf16x8 pack_bf16x8(const f32x4& lo, const f32x4& hi) {

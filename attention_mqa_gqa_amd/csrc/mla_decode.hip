@@ -95,21 +95,24 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
     // are masked.
     constexpr int kCopiesPerWave = (kKT + kRopeB / 1024) / kNW;
     static_assert(kCopiesPerWave * kNW == kKT + kRopeB / 1024, "copies must split evenly over the waves");
-    auto issue = [&](int tile) {
+    // copy i (0 .. 8) of this wave for tile `tile`
+    auto issue_one = [&](int tile, int i) {
         const uint32_t st = lds_base + (uint32_t)((tile % kNS) * kStageB);
         const int row0 = begin + tile * kKT;
-#pragma unroll
-        for (int i = 0; i < kKT / kNW; ++i) {
+        if (i < kKT / kNW) {
             const int u = i * kNW + w;               // wave-uniform latent row
             const int key = min(row0 + u, end - 1);
             copy16_to_lds_async(KVb + (size_t)key * kDK, lane16, st + (uint32_t)(layout::mla_lat_pos(u) * kLatRowB));
-        }
-        {
+        } else {
             const int r = 8 * w + (lane >> 3);       // RoPE row of this lane
             const int c = (lane & 7) ^ layout::mla_rope_swz(r);
             const int key = min(row0 + r, end - 1);
             copy16_to_lds_async(KVb, (uint32_t)key * (kDK * 2u) + (uint32_t)(kDC * 2 + c * 16), st + (uint32_t)(kLatB + w * 1024));
         }
+    };
+    auto issue = [&](int tile) {
+#pragma unroll
+        for (int i = 0; i < kCopiesPerWave; ++i) issue_one(tile, i);
     };
 
     // score operand offsets (bytes within a stage)
@@ -170,26 +173,24 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
                 if (ks + PF < KS) abuf[ks % PF] = kread(st, ks + PF);
                 s = mfma_32x32x16(a, qb[ks], s);
             }
+            sched_reads_ahead<PF, KS - PF>();
         }
 
         // ---- online softmax of heads 32w + n (keys 8(i/4) + 4h2 + i%4) ---------
+        // the scale is > 0, so the row max is taken on the raw scores and
+        // the scale folds into the exponent: p = 2^(s * c - m)
         const int row0 = begin + it * kKT;
         float mloc = -INFINITY;
         if (row0 + kKT > end) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int key = row0 + 8 * (i >> 2) + 4 * h2 + (i & 3);
-                s[i] = key < end ? s[i] * scale_log2 : -INFINITY;
-                mloc = fmaxf(mloc, s[i]);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                s[i] *= scale_log2;
-                mloc = fmaxf(mloc, s[i]);
+                if (key >= end) s[i] = -INFINITY;
             }
         }
-        const float mx = max_over_halves(mloc);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, s[i]);
+        const float mx = max_over_halves(mloc) * scale_log2;
         float alpha = 1.f;
         if (mx > m_run + kRescaleSlack) {
             const float mnew = fmaxf(m_run, mx);
@@ -200,7 +201,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
         float lsum = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            s[i] = fast_exp2(s[i] - m_run);
+            s[i] = fast_exp2(fmaf(s[i], scale_log2, -m_run));
             lsum += s[i];
         }
         l_run += lsum;
@@ -220,10 +221,26 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
         // tile it+1 has landed (nothing later was issued yet)
         wait_vmcnt<0>();
         __syncthreads();
-        if (it + 2 < n_tiles) issue(it + 2);
+        const bool copy_next = it + 2 < n_tiles;
 
         // ---- O^T += V^T P^T for value dims 128w .. 128w+127, all heads ------------
+        // 8 steps (kp, mt), each one V^T operand x 4 P^T operands.  The
+        // MFMAs are opaque to the scheduler, so the software pipeline is
+        // pinned with scheduling fences: V^T reads run two steps ahead and
+        // the P^T operands of kp = 1 are read during kp = 0.
         {
+            const char* pl = pbuf + (it & 1) * kPB;
+            auto pread = [&](int kp, int nt) {
+                const int hh = 32 * nt + n;
+                return *(const bf16x8*)(pl + hh * 64 + (((2 * kp + h2) ^ layout::ptile_swz(hh)) * 16));
+            };
+            constexpr int NSTEP = 2 * MT;
+            bf16x8 pb[2][NT];
+            bf16x8 va[3];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) pb[0][nt] = pread(0, nt);
+            va[0] = vread(st, 0, 0);
+            va[1] = vread(st, 0, 1);
             const float* al = alpha_buf + (it & 1) * kHMAX;
             float a4[NT];
             bool need = false;
@@ -232,32 +249,33 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
                 a4[nt] = al[32 * nt + n];
                 need |= a4[nt] != 1.f;
             }
+            // The copies of tile it+2 go out while the reads above are in
+            // flight: the memory pipeline takes one 1 KB copy at a time, so
+            // the issuing wave waits here either way.
+            if (copy_next) issue(it + 2);
             if (__any(need)) {
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt) scale_acc(o[mt][nt], a4[nt]);
             }
-            const char* pl = pbuf + (it & 1) * kPB;
 #pragma unroll
-            for (int kp = 0; kp < 2; ++kp) {
-                bf16x8 pb[NT];
+            for (int stp = 0; stp < NSTEP; ++stp) {
+                if (stp + 2 < NSTEP) va[(stp + 2) % 3] = vread(st, (stp + 2) / MT, (stp + 2) % MT);
+                if (stp == 1) {
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const int hh = 32 * nt + n;
-                    pb[nt] = *(const bf16x8*)(pl + hh * 64 + (((2 * kp + h2) ^ layout::ptile_swz(hh)) * 16));
+                    for (int nt = 0; nt < NT; ++nt) pb[1][nt] = pread(1, nt);
                 }
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    const bf16x8 va = vread(st, kp, mt);
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) o[mt][nt] = mfma_32x32x16(va, pb[nt], o[mt][nt]);
-                }
+                for (int nt = 0; nt < NT; ++nt) mfma_32x32x16_acc(va[stp % 3], pb[stp / MT][nt], o[stp % MT][nt]);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
 
     // ---- partials: unnormalised O^T slices, (m, l) per head ---------------------
+    mfma_acc_drain();
     const float l_tot = sum_over_halves(l_run);
     if (head_ok && h2 == 0) {
         const size_t prow = ((size_t)b * H + head) * n_split + s_idx;

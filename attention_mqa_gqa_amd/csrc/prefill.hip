@@ -334,10 +334,6 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
         }
 #pragma unroll
         for (int i = KS / 2 + 16; i < KS; ++i) s_step(i);
-        // keep the score accumulator in VGPRs: the O^T accumulator fills
-        // the AGPRs at D = 512
-#pragma unroll
-        for (int nt = 0; nt < NR; ++nt) asm volatile("" : "+v"(s_nxt[nt]));
         bf16x8 pb[NR][KSP];
 #pragma unroll
         for (int nt = 0; nt < NR; ++nt) {
@@ -375,15 +371,15 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
                 if (st + PF < NSTEP) vbuf[st % PF] = *(const bf16x8*)vaddr(st + PF);
                 const int kp = st / MT_O, mt = st % MT_O;
 #pragma unroll
-                for (int nt = 0; nt < NR; ++nt) o[mt][nt] = mfma_32x32x16(a, pb[nt][kp], o[mt][nt]);
+                for (int nt = 0; nt < NR; ++nt) mfma_32x32x16_acc(a, pb[nt][kp], o[mt][nt]);
             }
-            if constexpr (NR == 1) sched_reads_ahead<PF, NSTEP - PF>();
         }
 #pragma unroll
         for (int nt = 0; nt < NR; ++nt) s_cur[nt] = s_nxt[nt];
     }
 
     // ---- epilogue: normalise, store ------------------------------------------
+    mfma_acc_drain();
 #pragma unroll
     for (int nt = 0; nt < NR; ++nt) {
         const float l = sum_over_halves(l_run[nt]);

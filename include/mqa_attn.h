@@ -82,7 +82,7 @@ const char* mqa_last_hip_error_name(void);
  *   lse [B, Hq, T] fp32 or NULL
  *   causal != 0: key j is visible to query i iff j <= i (square, top-left
  *   aligned: query i is the token at position i).
- *   scale: the factor on Q.K^T, normally 1/sqrt(D).  Must be finite.
+ *   scale: the factor on Q.K^T, normally 1/sqrt(D).  Must be finite and > 0.
  * Supported: Hq % Hkv == 0;
  *   in_dtype BF16 -> out_dtype BF16 or F32, D in {128, 512}, and the group
  *     size G = Hq/Hkv a power of two with G <= 128 (D=512) or G <= 256
@@ -135,7 +135,8 @@ int mqa_decode(const void* q, const void* k_cache, const void* v_cache,
  *   q_abs [B, H, 576]   kv_cache [B, max_len, 576]   out [B, H, 512]
  *   seq_lens int32[B] on the device, as for mqa_decode.
  *   lse [B, H] fp32 or NULL.
- *   scale: normally 1/sqrt(128 + 64), the original per-head q.k width.
+ *   scale: normally 1/sqrt(128 + 64), the original per-head q.k width;
+ *          finite and > 0.
  * Supported: dtype BF16, out_dtype BF16 or F32, H a multiple of 16, H <= 128.
  * Workspace: `mla_decode_workspace_size()` bytes.
  */

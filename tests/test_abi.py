@@ -53,6 +53,8 @@ def test_prefill_rejections():
     assert _prefill(Hq=0) == INVALID
     assert _prefill(scale=float("inf")) == INVALID
     assert _prefill(scale=float("nan")) == INVALID
+    assert _prefill(scale=0.0) == INVALID                # softmax scale must be > 0
+    assert _prefill(scale=-0.05) == INVALID
     assert _prefill(din=7) == INVALID
     assert _prefill(q=None) == INVALID
     assert _prefill(out=MIS) == INVALID
@@ -89,6 +91,7 @@ def test_decode_rejections():
     assert _decode(sl=None) == INVALID
     assert _decode(sl=ctypes.c_void_p(4098)) == INVALID
     assert _decode(L=0) == INVALID
+    assert _decode(scale=0.0) == INVALID
     assert _decode(dt=F32, dout=F32) == UNSUPPORTED
     assert _decode(D=256) == UNSUPPORTED
     assert _decode(Hq=64, Hkv=2) == UNSUPPORTED          # group of 32 > 16 MFMA columns
@@ -107,6 +110,7 @@ def _mla(q=P, kv=P, sl=P, out=P, lse=None, B=32, H=128, L=32768, scale=0.072, dt
 def test_mla_rejections():
     assert _mla(H=0) == INVALID
     assert _mla(kv=MIS) == INVALID
+    assert _mla(scale=-1.0) == INVALID
     assert _mla(H=24) == UNSUPPORTED
     assert _mla(H=256) == UNSUPPORTED
     assert _mla(dt=F32) == UNSUPPORTED
