@@ -2,22 +2,31 @@
 
 One step = one pass of every entry point over its full-size synthetic
 workload, inputs already resident in HBM:
-  * mqa_prefill          causal MQA, B=2, Hq=16, Hkv=1, T=4096, d=512, bf16
-  * mqa_decode           MQA, batch 64, Hq=16, Hkv=1, d=512, cache 8192, bf16
+  * mqa_prefill          causal MQA, B=2, Hq=16, Hkv=1, T=4096, d=512
+  * mqa_decode           MQA, batch 64, Hq=16, Hkv=1, d=512, cache 8192
+  * mqa_prefill          causal GQA, B=1, Hq=64, Hkv=8, T=8192, d=128
+  * mqa_decode           GQA, batch 128, Hq=64, Hkv=8, d=128, cache
+                         lengths uniform in [1024, 16384]
   * mla_decode_absorbed  batch 32, H=128, latent 576 (V = first 512), ctx 32768
+all bf16 in, fp32 accumulation, bf16 out.
 
-Every launch is bracketed with HIP events on the stream it runs on.  The
-headline `value` is the causal-prefill TFLOP/s (visible query/key pairs
-only); the decode KV-read GB/s and the MLA figures sit beside it, each with
-its roofline.  `cpu_baseline` times the fp64 numpy oracle on a bounded
-sample on the host cores.
+Every call is bracketed with HIP events on the stream it is launched on.
+The headline `value` is the causal MQA prefill TFLOP/s (visible query/key
+pairs only, 4 d flops per pair); the other workloads sit beside it, each
+with its roofline.  `roofline.traffic` is the HBM traffic per call measured
+with rocprofv3 counters (profiles/traffic.json), reported only while the
+kernel sources still hash to the value recorded with the counters.
+`cpu_baseline` times the fp64 numpy oracle on a bounded sample on the host
+cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--only name,name] [--copy-calibration MIB]
 """
 
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -32,10 +41,16 @@ if ROOT not in sys.path:
 METRIC = "causal prefill TFLOP/s + decode KV-read GB/s, MQA Hq=16 d=512 bf16"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
-PREFILL = dict(B=2, Hq=16, Hkv=1, T=4096, D=512)
-DECODE = dict(B=64, Hq=16, Hkv=1, L=8192, D=512)
-MLA = dict(B=32, H=128, L=32768, DK=576, DV=512)
+# name -> role in the record; shapes come from synthetic.WORKLOADS
+ORDER = (
+    ("mqa_prefill_bf16_b2_t4096", "headline"),
+    ("mqa_decode_bf16_b64_l8192", "decode_kv_read"),
+    ("gqa_prefill_bf16_b1_t8192", "gqa_prefill"),
+    ("gqa_decode_bf16_b128_l1024to16384", "gqa_decode"),
+    ("mla_decode_bf16_b32_l32768", "mla_decode"),
+)
 
 
 def prefill_flops(B, Hq, T, D, causal=True, **_):
@@ -43,22 +58,56 @@ def prefill_flops(B, Hq, T, D, causal=True, **_):
     return B * Hq * pairs * 2 * (D + D)
 
 
+def prefill_bytes(B, Hq, Hkv, T, D, **_):
+    return (2 * B * Hq * T * D + 2 * B * Hkv * T * D) * 2      # q, out, k, v (bf16)
+
+
 def decode_bytes(B, Hq, Hkv, D, seq_lens, **_):
     kv = int(np.sum(seq_lens)) * Hkv * 2 * D * 2
     return kv + B * Hq * D * 2 * 2          # + q and out (bf16)
 
 
-def mla_bytes(B, H, DK, DV, seq_lens, **_):
-    return int(np.sum(seq_lens)) * DK * 2 + B * H * DK * 2 + B * H * DV * 2
+def decode_flops(Hq, D, seq_lens, **_):
+    return int(np.sum(seq_lens)) * Hq * 2 * (D + D)
 
 
-def mla_flops(B, H, DK, DV, seq_lens, **_):
-    return int(np.sum(seq_lens)) * H * 2 * (DK + DV)
+def mla_bytes(B, H, D, seq_lens, DV=512, **_):
+    return int(np.sum(seq_lens)) * D * 2 + B * H * D * 2 + B * H * DV * 2
 
 
-def roofline(bound, achieved, peak, unit):
+def mla_flops(H, D, seq_lens, DV=512, **_):
+    return int(np.sum(seq_lens)) * H * 2 * (D + DV)
+
+
+def source_hash():
+    """sha256 over the kernel sources and the ABI header (what the counters
+    were taken on)."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "attention_mqa_gqa_amd", "csrc")
+    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc) if f.endswith((".hip", ".hpp")))
+    files.append(os.path.join(ROOT, "include", "mqa_attn.h"))
+    files.append(os.path.join(ROOT, "attention_mqa_gqa_amd", "build.py"))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def load_traffic():
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return {}
+    if t.get("source_sha256") != source_hash():
+        return {}
+    return t.get("per_call_bytes", {})
+
+
+def roofline(bound, achieved, peak, unit, traffic=None):
     return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 4), "traffic": None}
+            "frac": round(achieved / peak, 4), "traffic": traffic}
 
 
 def blas_threads():
@@ -70,19 +119,32 @@ def blas_threads():
         return 1
 
 
-def cpu_baseline(q, k, v, scale):
-    """fp64 oracle on a bounded sample: all 16 heads of batch 0 of the
-    prefill workload (full 4096x4096 causal rows each)."""
+def cpu_baseline(q, k, v, scale, shape):
+    """fp64 oracle on a bounded sample: all heads of batch 0 of the MQA
+    prefill workload (full causal rows)."""
     import oracle
-    q0 = q.f32()[0:1]
-    k0 = k.f32()[0:1]
-    v0 = v.f32()[0:1]
     t0 = time.perf_counter()
-    oracle.prefill_ref(q0, k0, v0, scale, True)
+    oracle.prefill_ref(q.f32()[0:1], k.f32()[0:1], v.f32()[0:1], scale, True)
     dt = time.perf_counter() - t0
-    fl = prefill_flops(1, PREFILL["Hq"], PREFILL["T"], PREFILL["D"])
+    fl = prefill_flops(1, shape["Hq"], shape["T"], shape["D"])
     return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
-            "sample": f"causal MQA prefill, batch 0 of 2 (16 heads x T=4096 x d=512), fp64 numpy, {dt:.1f} s"}
+            "sample": f"causal MQA prefill, batch 0 of {shape['B']} ({shape['Hq']} heads x T={shape['T']} "
+                      f"x d={shape['D']}), fp64 numpy, {dt:.1f} s"}
+
+
+def copy_calibration(mib, reps):
+    """A plain device copy of known size (for scaling the HBM counters)."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read_per_call": n, "bytes_written_per_call": n, "calls": reps}}))
+    return 0
 
 
 def main():
@@ -91,67 +153,89 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default="", help="comma-separated workload names (default: all)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: every kernel here runs on a single MI355X "
-              "(the multi-GPU sharding is a design note, not built). Run with --gpus 1.", file=sys.stderr)
+              "(sharding across GPUs is a design note, not built). Run with --gpus 1.", file=sys.stderr)
         return 2
+    if args.copy_calibration:
+        return copy_calibration(args.copy_calibration, max(args.steps, 1))
 
     import torch
     import attention_mqa_gqa_amd as mqa
-    from synthetic import decode_inputs, mla_inputs, prefill_inputs
+    from synthetic import WORKLOADS, decode_inputs, mla_inputs, prefill_inputs
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    only = [s for s in args.only.split(",") if s]
+    names = [n for n, _ in ORDER if not only or n in only]
 
     def to_dev(t):
         if t.dtype == "bf16":
             return torch.from_numpy(np.ascontiguousarray(t.data).view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(np.ascontiguousarray(t.data)).to(dev)
 
+    calls, work, host = {}, {}, {}
     t_gen = time.perf_counter()
-    pq, pk, pv = prefill_inputs(PREFILL["B"], PREFILL["Hq"], PREFILL["Hkv"], PREFILL["T"], PREFILL["D"], "bf16", seed=0)
-    d_pq, d_pk, d_pv = to_dev(pq), to_dev(pk), to_dev(pv)
-    dq, dk, dv, dsl = decode_inputs(DECODE["B"], DECODE["Hq"], DECODE["Hkv"], DECODE["L"], DECODE["D"], "bf16", seed=0)
-    d_dq, d_dk, d_dv, d_dsl = to_dev(dq), to_dev(dk), to_dev(dv), torch.from_numpy(dsl).to(dev)
-    del dk, dv
-    mq, mkv, msl = mla_inputs(MLA["B"], MLA["H"], MLA["L"], MLA["DK"], "bf16", seed=0)
-    d_mq, d_mkv, d_msl = to_dev(mq), to_dev(mkv), torch.from_numpy(msl).to(dev)
-    del mkv
-    print(f"[bench] inputs ready in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
-
-    scale_p = PREFILL["D"] ** -0.5
-    scale_m = 192 ** -0.5
-    # outputs and workspaces allocated once, outside the timed region
-    p_out = torch.empty((PREFILL["B"], PREFILL["Hq"], PREFILL["T"], PREFILL["D"]), dtype=torch.bfloat16, device=dev)
-    p_ws = torch.empty(mqa.mqa_prefill_workspace_size(PREFILL["B"], PREFILL["Hq"], PREFILL["Hkv"], PREFILL["T"],
-                                                      PREFILL["D"], mqa.DTYPE_BF16), dtype=torch.uint8, device=dev)
-    d_out = torch.empty((DECODE["B"], DECODE["Hq"], DECODE["D"]), dtype=torch.bfloat16, device=dev)
-    d_ws = torch.empty(mqa.mqa_decode_workspace_size(DECODE["B"], DECODE["Hq"], DECODE["Hkv"], DECODE["L"], DECODE["D"]),
-                       dtype=torch.uint8, device=dev)
-    m_out = torch.empty((MLA["B"], MLA["H"], MLA["DV"]), dtype=torch.bfloat16, device=dev)
-    m_ws = torch.empty(mqa.mla_decode_workspace_size(MLA["B"], MLA["H"], MLA["L"]), dtype=torch.uint8, device=dev)
+    for name in names:
+        wl = WORKLOADS[name]
+        s = dict(wl.shape)
+        if wl.kind == "prefill":
+            q, k, v = prefill_inputs(s["B"], s["Hq"], s["Hkv"], s["T"], s["D"], "bf16", seed=0)
+            dq, dk, dv = to_dev(q), to_dev(k), to_dev(v)
+            out = torch.empty((s["B"], s["Hq"], s["T"], s["D"]), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(max(1, mqa.mqa_prefill_workspace_size(s["B"], s["Hq"], s["Hkv"], s["T"], s["D"],
+                                                                   mqa.DTYPE_BF16)), dtype=torch.uint8, device=dev)
+            sc = s["D"] ** -0.5
+            calls[name] = (lambda dq=dq, dk=dk, dv=dv, out=out, ws=ws, sc=sc:
+                           mqa.mqa_prefill(dq, dk, dv, causal=True, scale=sc, out=out, workspace=ws))
+            work[name] = dict(flops=prefill_flops(**s), bytes=prefill_bytes(**s), bound="mfma", shape=s)
+            if name == ORDER[0][0]:
+                host[name] = (q, k, v, sc, s)
+        elif wl.kind == "decode":
+            q, k, v, sl = decode_inputs(s["B"], s["Hq"], s["Hkv"], s["L"], s["D"], "bf16", seed=0,
+                                        lengths=s.get("lengths"))
+            dq, dk, dv, dsl = to_dev(q), to_dev(k), to_dev(v), torch.from_numpy(sl).to(dev)
+            del k, v
+            out = torch.empty((s["B"], s["Hq"], s["D"]), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(mqa.mqa_decode_workspace_size(s["B"], s["Hq"], s["Hkv"], s["L"], s["D"]),
+                             dtype=torch.uint8, device=dev)
+            sc = s["D"] ** -0.5
+            calls[name] = (lambda dq=dq, dk=dk, dv=dv, dsl=dsl, out=out, ws=ws, sc=sc:
+                           mqa.mqa_decode(dq, dk, dv, dsl, scale=sc, out=out, workspace=ws))
+            work[name] = dict(flops=decode_flops(s["Hq"], s["D"], sl),
+                              bytes=decode_bytes(s["B"], s["Hq"], s["Hkv"], s["D"], sl), bound="hbm", shape=s,
+                              mean_len=float(np.mean(sl)))
+        else:
+            q, kv, sl = mla_inputs(s["B"], s["H"], s["L"], s["D"], "bf16", seed=0)
+            dq, dkv, dsl = to_dev(q), to_dev(kv), torch.from_numpy(sl).to(dev)
+            del kv
+            out = torch.empty((s["B"], s["H"], 512), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(mqa.mla_decode_workspace_size(s["B"], s["H"], s["L"]), dtype=torch.uint8, device=dev)
+            sc = 192 ** -0.5
+            calls[name] = (lambda dq=dq, dkv=dkv, dsl=dsl, out=out, ws=ws, sc=sc:
+                           mqa.mla_decode_absorbed(dq, dkv, dsl, scale=sc, out=out, workspace=ws))
+            work[name] = dict(flops=mla_flops(s["H"], s["D"], sl), bytes=mla_bytes(s["B"], s["H"], s["D"], sl),
+                              bound="hbm", shape=s)
+        print(f"[bench] {name} ready ({time.perf_counter() - t_gen:.1f} s)", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream(dev)
-    calls = {
-        "prefill": lambda: mqa.mqa_prefill(d_pq, d_pk, d_pv, causal=True, scale=scale_p, out=p_out, workspace=p_ws),
-        "decode": lambda: mqa.mqa_decode(d_dq, d_dk, d_dv, d_dsl, scale=scale_p, out=d_out, workspace=d_ws),
-        "mla": lambda: mqa.mla_decode_absorbed(d_mq, d_mkv, d_msl, scale=scale_m, out=m_out, workspace=m_ws),
-    }
 
     def step(events=None):
-        for name, fn in calls.items():
+        for name in names:
             if events is not None:
                 events[name][0].record(stream)
-            fn()
+            calls[name]()
             if events is not None:
                 events[name][1].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-
-    evs = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in calls}
+    evs = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
            for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -160,22 +244,35 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    ms = {n: np.array([e[n][0].elapsed_time(e[n][1]) for e in evs]) for n in calls}
-    mean = {n: float(v.mean()) for n, v in ms.items()}
-    med = {n: float(np.median(v)) for n, v in ms.items()}
+    traffic = load_traffic()
+    sub = {}
+    for name in names:
+        w = work[name]
+        ms = np.array([e[name][0].elapsed_time(e[name][1]) for e in evs])
+        mean = float(ms.mean())
+        tflops = w["flops"] / (mean * 1e-3) / 1e12
+        gbs = w["bytes"] / (mean * 1e-3) / 1e9
+        tr = traffic.get(name)
+        r = {"workload": name, "shape": {k: v for k, v in w["shape"].items()},
+             "ms": {"mean": round(mean, 4), "median": round(float(np.median(ms)), 4), "min": round(float(ms.min()), 4)},
+             "algorithmic_flops": w["flops"], "algorithmic_bytes": w["bytes"],
+             "tflops": round(tflops, 2), "gbs": round(gbs, 1)}
+        if w["bound"] == "mfma":
+            r["roofline"] = roofline("mfma", tflops, PEAK_BF16_TFLOPS, "TFLOP/s", tr)
+        else:
+            r["roofline"] = roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", tr)
+            if name.startswith("mla"):
+                r["roofline_mfma"] = roofline("mfma", tflops, PEAK_BF16_TFLOPS, "TFLOP/s", tr)
+        if "mean_len" in w:
+            r["mean_seq_len"] = w["mean_len"]
+        if r["shape"].get("lengths") is not None:
+            r["shape"]["lengths"] = list(r["shape"]["lengths"])
+        sub[name] = r
 
-    pfl = prefill_flops(**PREFILL)
-    p_tflops = pfl / (mean["prefill"] * 1e-3) / 1e12
-    dbytes = decode_bytes(DECODE["B"], DECODE["Hq"], DECODE["Hkv"], DECODE["D"], dsl)
-    d_gbs = dbytes / (mean["decode"] * 1e-3) / 1e9
-    mbytes = mla_bytes(MLA["B"], MLA["H"], MLA["DK"], MLA["DV"], msl)
-    mfl = mla_flops(MLA["B"], MLA["H"], MLA["DK"], MLA["DV"], msl)
-    m_gbs = mbytes / (mean["mla"] * 1e-3) / 1e9
-    m_tflops = mfl / (mean["mla"] * 1e-3) / 1e12
-
+    head = ORDER[0][0]
     rec = {
         "metric": METRIC,
-        "value": round(p_tflops, 2),
+        "value": sub[head]["tflops"] if head in sub else None,
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -188,38 +285,23 @@ def main():
         "data": "synthetic (seeded iid N(0,1), bf16-rounded)",
         "config": {
             "workload": "mqa_prefill causal B=2 Hq=16 Hkv=1 T=4096 d=512 bf16",
-            "global_batch": PREFILL["B"],
-            "seq_len": PREFILL["T"],
-            "heads": f"Hq={PREFILL['Hq']} Hkv={PREFILL['Hkv']}",
-            "head_dim": PREFILL["D"],
-            "step": "mqa_prefill + mqa_decode (B=64, L=8192) + mla_decode_absorbed (B=32, H=128, L=32768)",
+            "global_batch": 2,
+            "seq_len": 4096,
+            "heads": "Hq=16 Hkv=1",
+            "head_dim": 512,
+            "step": " + ".join(names),
         },
-        "prefill_ms": {"mean": round(mean["prefill"], 4), "median": round(med["prefill"], 4),
-                       "min": round(float(ms["prefill"].min()), 4)},
-        "roofline": roofline("mfma", p_tflops, PEAK_BF16_TFLOPS, "TFLOP/s"),
-        "decode_kv_read": {
-            "workload": "mqa_decode B=64 Hq=16 Hkv=1 d=512 L=8192 bf16",
-            "value": round(d_gbs, 1), "unit": "GB/s",
-            "ms": {"mean": round(mean["decode"], 4), "median": round(med["decode"], 4),
-                   "min": round(float(ms["decode"].min()), 4)},
-            "algorithmic_bytes": dbytes,
-            "roofline": roofline("hbm", d_gbs, PEAK_HBM_GBS, "GB/s"),
-        },
-        "mla_decode": {
-            "workload": "mla_decode_absorbed B=32 H=128 kv 576/512 L=32768 bf16",
-            "value": round(m_gbs, 1), "unit": "GB/s",
-            "tflops": round(m_tflops, 2),
-            "ms": {"mean": round(mean["mla"], 4), "median": round(med["mla"], 4),
-                   "min": round(float(ms["mla"].min()), 4)},
-            "algorithmic_bytes": mbytes, "algorithmic_flops": mfl,
-            "roofline": roofline("hbm", m_gbs, PEAK_HBM_GBS, "GB/s"),
-            "roofline_mfma": roofline("mfma", m_tflops, PEAK_BF16_TFLOPS, "TFLOP/s"),
-        },
-        "cpu_baseline": None,
+        "roofline": sub[head]["roofline"] if head in sub else None,
     }
-    if not args.no_cpu_baseline:
+    for name, role in ORDER:
+        if name in sub and role != "headline":
+            rec[role] = sub[name]
+    if head in sub:
+        rec["prefill"] = sub[head]
+    rec["cpu_baseline"] = None
+    if not args.no_cpu_baseline and head in host:
         print("[bench] timing the fp64 oracle on a sample ...", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(pq, pk, pv, scale_p)
+        rec["cpu_baseline"] = cpu_baseline(*host[head])
     print(json.dumps(rec), flush=True)
     return 0
 
