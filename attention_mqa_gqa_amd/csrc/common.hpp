@@ -113,6 +113,14 @@ constexpr uint32_t kSelHiHalves = 0x07060302u;  // {lo.h1, hi.h1}
 
 // Max / sum over the two lane halves l, l^32 (the two halves holding one
 // output column of a 32x32 MFMA tile).
+// max of three floats in one v_max3_f32 (fmaxf chains also emit a NaN-
+// quieting max per operand; scores here are never NaN)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 // v_permlane32_swap with both operands = v leaves, in every lane, v of that
 // lane and of its partner l ^ 32 in the two results (no LDS round trip).
 __device__ __forceinline__ float max_over_halves(float v) {

@@ -189,7 +189,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
             }
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, s[i]);
+        for (int i = 0; i < 8; ++i) mloc = max3f(mloc, s[2 * i], s[2 * i + 1]);
         const float mx = max_over_halves(mloc) * scale_log2;
         float alpha = 1.f;
         if (mx > m_run + kRescaleSlack) {

@@ -236,6 +236,28 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
         }
     };
 
+    // Softmax pieces on one tile's scores (raw S^T accumulators; the scale
+    // is > 0, so row maxima are taken on raw scores and the scale folds
+    // into the exponent).  Key of accumulator i of lane half h2 within the
+    // tile: layout::c32_index(h2, i); row nt of this lane: token row_tok[nt].
+    auto mask_tile = [&](f32x16 (&sc)[NR], int tile) {
+        const int j0 = tile * KT;
+#pragma unroll
+        for (int nt = 0; nt < NR; ++nt) {
+            const int lim = (CAUSAL ? min(row_tok[nt], T - 1) : T - 1) - j0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (layout::c32_index(h2, i) > lim) sc[nt][i] = -INFINITY;
+        }
+    };
+    // does any row of this wave see a masked key in `tile`?
+    const int wave_tok_min = t0 + (w * RW) / G;
+    auto tile_masked = [&](int tile) {
+        const int last_key = tile * KT + KT - 1;
+        return last_key >= T || (CAUSAL && last_key > wave_tok_min);
+    };
+    const float c = scale_log2;
+
     // prologue: copies K(0), K(1), V(0); S(0); then K(2) once every wave is
     // done with K(0).  Global copy order: K0 K1 V0 K2 | V1 K3 | V2 K4 | ...
     issue_k(0);
@@ -243,119 +265,102 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     issue_v(0);
     wait_vmcnt_of<LH, LH>(n_tiles > 1 ? 2 * LH : LH);   // K(0) has landed
     __syncthreads();
-    f32x16 s_cur[NR];
+    f32x16 sA[NR], sB[NR];
 #pragma unroll
-    for (int nt = 0; nt < NR; ++nt) s_cur[nt] = f32x16{};
-    s_all(s_cur, smem);
+    for (int nt = 0; nt < NR; ++nt) sA[nt] = f32x16{};
+    s_all(sA, smem);
     __syncthreads();
     if (n_tiles > 2) issue_k(2);
+    if (tile_masked(0)) mask_tile(sA, 0);
+#pragma unroll
+    for (int nt = 0; nt < NR; ++nt) {
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mloc = max3f(mloc, sA[nt][2 * i], sA[nt][2 * i + 1]);
+        m_run[nt] = max_over_halves(mloc) * c;
+    }
 
-    for (int it = 0; it < n_tiles; ++it) {
+    // Iteration t (scores of tile t in sc, masked, row max folded into m_run):
+    //   phase A: S(t+1) MFMAs, with the exponentials, row sums and bf16
+    //            packing of P(t) placed between them;
+    //   phase B: P(t).V(t) MFMAs, with the masking and row max of S(t+1)
+    //            between them; then the (rare) lazy rescale for tile t+1.
+    // Each phase is a fixed sequence of chunks separated by scheduling
+    // fences, so MFMA latency is filled with this wave's VALU work.  Right
+    // after barrier A, V(t+1) is copied into the stage of V(t-1); right
+    // after barrier B, K(t+3) into the stage of K(t+1).  Copies are issued
+    // in the order they are consumed, so in-order vmcnt waits are exact.
+    // The score buffers alternate between sA and sB (loop unrolled by 2).
+    constexpr int NSTEP_PV = KSP * MT_O;
+    auto body = [&](int it, f32x16 (&sc)[NR], f32x16 (&sn)[NR]) {
         const bool has_next = it + 1 < n_tiles;
         const bool has_next2 = it + 2 < n_tiles;
         // K(it+1) has landed; V(it) and K(it+2) may still be in flight
         if (has_next) wait_vmcnt_of<LH, LH>(LH + (has_next2 ? LH : 0));
+        __builtin_amdgcn_sched_barrier(0);
         __syncthreads();                                       // barrier A
-        if (has_next) issue_v(it + 1);
 
-        f32x16 s_nxt[NR];
-#pragma unroll
-        for (int nt = 0; nt < NR; ++nt) s_nxt[nt] = f32x16{};
-        // S(it+1) is computed unconditionally so that it shares a basic block
-        // with the softmax of S(it) (on the last tile it reads a stale but
-        // valid K stage and is discarded).  The two are interleaved by hand:
-        // every step issues one S MFMA (operand read PF steps ahead) and the
-        // softmax work of one score element, so the VALU work fills the MFMA
-        // shadow of this wave.
+        // ---- phase A: S(it+1) (unconditionally: on the last tile it reads a
+        // stale but valid K stage and is discarded) | exp of S(it) ----------
+        // The first K operand reads go out before the V(it+1) copies, whose
+        // issue then covers their latency.
         const char* kst = smem + ((it + 1) & 1) * KSTAGE_B;
-        bf16x8 abuf[PF];
 #pragma unroll
-        for (int j = 0; j < PF; ++j) abuf[j] = kread(kst, j);
-        auto s_step = [&](int ks) {
-            const bf16x8 a = abuf[ks % PF];
-            if (ks + PF < KS) abuf[ks % PF] = kread(kst, ks + PF);
-#pragma unroll
-            for (int nt = 0; nt < NR; ++nt) s_nxt[nt] = mfma_32x32x16(a, qb[nt][ks], s_nxt[nt]);
-        };
-        static_assert(KS >= 32 || D == 128, "interleave expects 32 steps at D = 512");
-
-        // first half: scale, mask (branch-free) and row max of S(it)
-        const int j0 = it * KT;
-        int lim[NR];
-        float mloc[NR];
-#pragma unroll
-        for (int nt = 0; nt < NR; ++nt) {
-            lim[nt] = (CAUSAL ? min(row_tok[nt], T - 1) : T - 1) - j0;
-            mloc[nt] = -INFINITY;
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            if (i < KS / 2) s_step(i);
-#pragma unroll
-            for (int nt = 0; nt < NR; ++nt) {
-                const float v = layout::c32_index(h2, i) <= lim[nt] ? s_cur[nt][i] * scale_log2 : -INFINITY;
-                s_cur[nt][i] = v;
-                mloc[nt] = fmaxf(mloc[nt], v);
-            }
-        }
-#pragma unroll
-        for (int i = 16; i < KS / 2; ++i) s_step(i);
-        float mx[NR];
-        bool need = false;
-#pragma unroll
-        for (int nt = 0; nt < NR; ++nt) {
-            mx[nt] = max_over_halves(mloc[nt]);
-            need |= mx[nt] > m_run[nt] + kRescaleSlack;
-        }
-        if (__any(need)) {
-#pragma unroll
-            for (int nt = 0; nt < NR; ++nt) {
-                const float mnew = fmaxf(m_run[nt], mx[nt]);
-                const float alpha = (m_run[nt] == -INFINITY) ? 0.f : fast_exp2(m_run[nt] - mnew);
-                m_run[nt] = mnew;
-                l_run[nt] *= alpha;
-#pragma unroll
-                for (int mt = 0; mt < MT_O; ++mt) scale_acc(o[mt][nt], alpha);
-            }
-        }
-        // second half: exp, row sum, pack P(it)
+        for (int nt = 0; nt < NR; ++nt) sn[nt] = f32x16{};
         float lsum[NR];
 #pragma unroll
         for (int nt = 0; nt < NR; ++nt) lsum[nt] = 0.f;
+        {
+            bf16x8 abuf[PF];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            if (KS / 2 + i < KS) s_step(KS / 2 + i);
+            for (int j = 0; j < PF; ++j) abuf[j] = kread(kst, j);
+            if (has_next) issue_v(it + 1);
 #pragma unroll
-            for (int nt = 0; nt < NR; ++nt) {
-                const float p = fast_exp2(s_cur[nt][i] - m_run[nt]);
-                s_cur[nt][i] = p;
-                lsum[nt] += p;
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 a = abuf[ks % PF];
+                if (ks + PF < KS) abuf[ks % PF] = kread(kst, ks + PF);
+#pragma unroll
+                for (int nt = 0; nt < NR; ++nt) sn[nt] = mfma_32x32x16(a, qb[nt][ks], sn[nt]);
+#pragma unroll
+                for (int i = ks * 16 / KS; i < (ks + 1) * 16 / KS; ++i) {
+#pragma unroll
+                    for (int nt = 0; nt < NR; ++nt) {
+                        const float pr = fast_exp2(fmaf(sc[nt][i], c, -m_run[nt]));
+                        sc[nt][i] = pr;
+                        lsum[nt] += pr;
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
-#pragma unroll
-        for (int i = KS / 2 + 16; i < KS; ++i) s_step(i);
         bf16x8 pb[NR][KSP];
 #pragma unroll
         for (int nt = 0; nt < NR; ++nt) {
             l_run[nt] += lsum[nt];
+            asm volatile("" : "+v"(l_run[nt]));
 #pragma unroll
             for (int kp = 0; kp < KSP; ++kp) {
-                f32x4 lo = {s_cur[nt][8 * kp + 0], s_cur[nt][8 * kp + 1], s_cur[nt][8 * kp + 2], s_cur[nt][8 * kp + 3]};
-                f32x4 hi = {s_cur[nt][8 * kp + 4], s_cur[nt][8 * kp + 5], s_cur[nt][8 * kp + 6], s_cur[nt][8 * kp + 7]};
+                f32x4 lo = {sc[nt][8 * kp + 0], sc[nt][8 * kp + 1], sc[nt][8 * kp + 2], sc[nt][8 * kp + 3]};
+                f32x4 hi = {sc[nt][8 * kp + 4], sc[nt][8 * kp + 5], sc[nt][8 * kp + 6], sc[nt][8 * kp + 7]};
                 pb[nt][kp] = pack_bf16x8(lo, hi);
+                // keeps the exponentials in phase A: without a use here the
+                // compiler sinks them past barrier B to the P.V MFMAs
+                asm volatile("" : "+v"(pb[nt][kp]));
             }
         }
 
         // V(it) has landed (K(it+2) and V(it+1) may still be in flight)
         wait_vmcnt_of<LH, LH>((has_next2 ? LH : 0) + (has_next ? LH : 0));
+        __builtin_amdgcn_sched_barrier(0);
         __syncthreads();                                       // barrier B
-        if (it + 3 < n_tiles) issue_k(it + 3);
 
-        // ---- O^T += V^T P^T --------------------------------------------------
-        // contraction step outer, head-dim tile inner; V^T operand reads run
-        // PF steps ahead.
+        // ---- phase B: O^T += V^T P^T (contraction step outer, head-dim tile
+        // inner, V^T reads PF steps ahead) | row max of S(it+1) --------------
+        // As in phase A, the first operand reads precede the copies.
+        float mloc[NR];
+#pragma unroll
+        for (int nt = 0; nt < NR; ++nt) mloc[nt] = -INFINITY;
         {
-            constexpr int NSTEP = KSP * MT_O;
             const char* vl = smem + 2 * KSTAGE_B + (it & 1) * VSTAGE_B;
             bf16x8 vbuf[PF];
             auto vaddr = [&](int step) {
@@ -365,17 +370,49 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
             };
 #pragma unroll
             for (int st = 0; st < PF; ++st) vbuf[st] = *(const bf16x8*)vaddr(st);
+            if (it + 3 < n_tiles) issue_k(it + 3);
+            if (has_next && tile_masked(it + 1)) mask_tile(sn, it + 1);
 #pragma unroll
-            for (int st = 0; st < NSTEP; ++st) {
+            for (int st = 0; st < NSTEP_PV; ++st) {
                 const bf16x8 a = vbuf[st % PF];
-                if (st + PF < NSTEP) vbuf[st % PF] = *(const bf16x8*)vaddr(st + PF);
+                if (st + PF < NSTEP_PV) vbuf[st % PF] = *(const bf16x8*)vaddr(st + PF);
                 const int kp = st / MT_O, mt = st % MT_O;
 #pragma unroll
                 for (int nt = 0; nt < NR; ++nt) mfma_32x32x16_acc(a, pb[nt][kp], o[mt][nt]);
+                // two scores per max3
+#pragma unroll
+                for (int i = st * 8 / NSTEP_PV; i < (st + 1) * 8 / NSTEP_PV; ++i) {
+#pragma unroll
+                    for (int nt = 0; nt < NR; ++nt) mloc[nt] = max3f(mloc[nt], sn[nt][2 * i], sn[nt][2 * i + 1]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
+        // lazy rescale for tile it+1: only when a row max grew by more than
+        // 2^kRescaleSlack (after the P.V MFMAs of this tile have drained)
+        float mx[NR];
+        bool need = false;
 #pragma unroll
-        for (int nt = 0; nt < NR; ++nt) s_cur[nt] = s_nxt[nt];
+        for (int nt = 0; nt < NR; ++nt) {
+            mx[nt] = max_over_halves(mloc[nt]) * c;
+            need |= mx[nt] > m_run[nt] + kRescaleSlack;
+        }
+        if (__any(need && has_next)) {
+            mfma_acc_drain();
+#pragma unroll
+            for (int nt = 0; nt < NR; ++nt) {
+                const float mnew = fmaxf(m_run[nt], mx[nt]);
+                const float alpha = fast_exp2(m_run[nt] - mnew);
+                m_run[nt] = mnew;
+                l_run[nt] *= alpha;
+#pragma unroll
+                for (int mt = 0; mt < MT_O; ++mt) scale_acc(o[mt][nt], alpha);
+            }
+        }
+    };
+    for (int it = 0; it < n_tiles; it += 2) {
+        body(it, sA, sB);
+        if (it + 1 < n_tiles) body(it + 1, sB, sA);
     }
 
     // ---- epilogue: normalise, store ------------------------------------------
