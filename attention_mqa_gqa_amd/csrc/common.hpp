@@ -154,6 +154,11 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const void* p) {
 }
 
 __device__ __forceinline__ u32x4 ldg16(const void* p) { return *(const u32x4*)p; }
+// Streaming 16-byte load (non-temporal hint): data read once, e.g. a KV cache.
+__device__ __forceinline__ u32x4 ldg16_stream(const void* p) { return __builtin_nontemporal_load((const u32x4*)p); }
+__device__ __forceinline__ bf16x8 ldg_bf16x8_stream(const void* p) {
+    return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load((const u32x4*)p));
+}
 __device__ __forceinline__ bf16x8 ldg_bf16x8(const void* p) { return *(const bf16x8*)p; }
 
 // Asynchronous 16-byte copy global -> LDS.  Every lane supplies its own

@@ -17,6 +17,7 @@
 //   * a second kernel merges the splits of each row by log-sum-exp in a fixed
 //     order, so the result is deterministic (no float atomics; lzwjava §4
 //     on ordering and determinism).
+// The cache streams with non-temporal loads (each row is read once).
 // Cache rows at or beyond seq_lens[b] are never read.
 #include "common.hpp"
 #include "layout.hpp"
@@ -74,22 +75,43 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(
     for (int mt = 0; mt < MT_O; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
 
-    for (int k0 = k_begin; k0 < k_end; k0 += STEP) {
-        bf16x8 ka[KSUB][KS];
-        u32x4 vr[KSUB][NSL][4];
+    // K rows of a step land directly in the A-operand layout of the S^T
+    // MFMA; V rows 16 bytes at a time.  Rows past k_end are clamped to the
+    // last valid row (and masked below).
+    bf16x8 ka[KSUB][KS];
+    u32x4 vr[KSUB][NSL][4];
+    auto load_k = [&](int k0) {
 #pragma unroll
         for (int sub = 0; sub < KSUB; ++sub) {
-            // K: row k0 + 16*sub + n, head dims 32ks + 8g.. (clamped inside the valid range)
             const int kr = min(k0 + 16 * sub + n, k_end - 1);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) ka[sub][ks] = ldg_bf16x8(Kbh + (size_t)kr * D + 32 * ks + 8 * g);
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16* src = Kbh + (size_t)kr * D + 32 * ks + 8 * g;
+                // streaming hint: faster for 1 KB rows, slower for 256-byte
+                // rows (two loads share each 128-byte line here)
+                ka[sub][ks] = (D >= 512) ? ldg_bf16x8_stream(src) : ldg_bf16x8(src);
+            }
+        }
+    };
+    auto load_v = [&](int k0) {
+#pragma unroll
+        for (int sub = 0; sub < KSUB; ++sub)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int vrow = min(k0 + 16 * sub + 4 * g + j, k_end - 1);
 #pragma unroll
-                for (int sl = 0; sl < NSL; ++sl) vr[sub][sl][j] = ldg16(Vbh + (size_t)vrow * D + (16 * sl + n) * 8);
+                for (int sl = 0; sl < NSL; ++sl) vr[sub][sl][j] = ldg16_stream(Vbh + (size_t)vrow * D + (16 * sl + n) * 8);
             }
-        }
+    };
+    // Software pipeline: the K rows of the next step load while this step's
+    // softmax and P.V run, and its V rows while the next scores run, so the
+    // wave always has one of the two streams in flight.
+    if (k_begin < k_end) {
+        load_k(k_begin);
+        load_v(k_begin);
+    }
+    for (int k0 = k_begin; k0 < k_end; k0 += STEP) {
+        const bool more = k0 + STEP < k_end;
         // S^T: lane group g holds keys k0 + 16 sub + 4g + i for head n
         f32x4 s[KSUB];
 #pragma unroll
@@ -98,6 +120,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) s[sub] = mfma_16x16x32(ka[sub][ks], qb[ks], s[sub]);
         }
+        if (more) load_k(k0 + STEP);
         float mloc = -INFINITY;
 #pragma unroll
         for (int sub = 0; sub < KSUB; ++sub) {
@@ -144,6 +167,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(
                 }
             }
         }
+        if (more) load_v(k0 + STEP);
     }
 
     // ---- merge the waves of this workgroup through LDS ------------------------
