@@ -191,6 +191,18 @@ __device__ __forceinline__ void copy16_to_lds_async(const void* base, uint32_t v
         : "memory", "m0");
 }
 
+// The same copy with the non-temporal hint, for data read exactly once
+// (an MLA latent cache streamed through LDS).
+__device__ __forceinline__ void copy16_to_lds_async_stream(const void* base, uint32_t voff, uint32_t lds_byte) {
+    asm volatile(
+        "s_nop 4\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %0, %1 nt"
+        :
+        : "v"(voff), "s"(base), "s"(lds_byte)
+        : "memory", "m0");
+}
+
 // Same, with up to VALU vector-ALU instructions (transcendentals included)
 // placed after each MFMA: lets independent softmax work fill the MFMA
 // shadow of a single wave.

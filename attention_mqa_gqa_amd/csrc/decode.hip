@@ -264,9 +264,10 @@ hipError_t merge_launch(const float* part_o, const float* part_ml, const int32_t
 }
 
 // ---------------------------------------------------------------------------
-// Plan: chunk = cache rows per workgroup.  Large enough that the partials
-// stay a small fraction of the cache bytes, small enough to give a few
-// hundred to a few thousand workgroups.
+// Plan: chunk = cache rows per workgroup.  About 1024 workgroups of the
+// longest sequence in total (fewer, longer chunks measured faster than more
+// splits: each workgroup pays a load latency before its first step and a
+// partial write), never under min_chunk rows.
 // ---------------------------------------------------------------------------
 static int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
@@ -274,7 +275,7 @@ DecodePlan decode_plan(int B, int Hkv, int max_len, int head_dim) {
     const long units = (long)B * Hkv;
     const int step = head_dim == 512 ? 4 * 16 : 4 * 64;      // NW * STEP
     const int min_chunk = head_dim == 512 ? 2048 : 1024;
-    const long target_wgs = head_dim == 512 ? 1024 : 4096;
+    const long target_wgs = 1024;
     long want = ((long)max_len * units + target_wgs - 1) / target_wgs;
     int chunk = (int)(want > max_len ? max_len : want);
     if (chunk < min_chunk) chunk = min_chunk;

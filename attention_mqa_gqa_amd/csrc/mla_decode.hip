@@ -11,7 +11,8 @@
 //   * one workgroup (4 waves, one per SIMD) = one (sequence, chunk of rows)
 //     and all (up to 128) heads;
 //   * 32-row tiles are copied global -> LDS with asynchronous direct-to-LDS
-//     loads, three stages deep (two tiles in flight);
+//     loads (non-temporal: each cached row is read once), three stages deep
+//     (two tiles in flight);
 //   * scores: wave w computes S^T = KV q_abs^T for heads 32w..32w+31 on
 //     v_mfma_f32_32x32x16_bf16 (36 contraction steps over the 576-wide
 //     row), then the online softmax of those heads;
@@ -102,12 +103,12 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
         if (i < kKT / kNW) {
             const int u = i * kNW + w;               // wave-uniform latent row
             const int key = min(row0 + u, end - 1);
-            copy16_to_lds_async(KVb + (size_t)key * kDK, lane16, st + (uint32_t)(layout::mla_lat_pos(u) * kLatRowB));
+            copy16_to_lds_async_stream(KVb + (size_t)key * kDK, lane16, st + (uint32_t)(layout::mla_lat_pos(u) * kLatRowB));
         } else {
             const int r = 8 * w + (lane >> 3);       // RoPE row of this lane
             const int c = (lane & 7) ^ layout::mla_rope_swz(r);
             const int key = min(row0 + r, end - 1);
-            copy16_to_lds_async(KVb, (uint32_t)key * (kDK * 2u) + (uint32_t)(kDC * 2 + c * 16), st + (uint32_t)(kLatB + w * 1024));
+            copy16_to_lds_async_stream(KVb, (uint32_t)key * (kDK * 2u) + (uint32_t)(kDC * 2 + c * 16), st + (uint32_t)(kLatB + w * 1024));
         }
     };
     auto issue = [&](int tile) {
