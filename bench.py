@@ -119,17 +119,23 @@ def blas_threads():
         return 1
 
 
-def cpu_baseline(q, k, v, scale, shape):
+def cpu_baseline(q, k, v, scale, shape, min_seconds=10.0):
     """fp64 oracle on a bounded sample: all heads of batch 0 of the MQA
-    prefill workload (full causal rows)."""
+    prefill workload (full causal rows), repeated until at least
+    `min_seconds` of host time have been spent (and at least once)."""
     import oracle
-    t0 = time.perf_counter()
-    oracle.prefill_ref(q.f32()[0:1], k.f32()[0:1], v.f32()[0:1], scale, True)
-    dt = time.perf_counter() - t0
-    fl = prefill_flops(1, shape["Hq"], shape["T"], shape["D"])
+    q0, k0, v0 = q.f32()[0:1], k.f32()[0:1], v.f32()[0:1]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.prefill_ref(q0, k0, v0, scale, True)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    fl = prefill_flops(1, shape["Hq"], shape["T"], shape["D"]) * reps
     return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
             "sample": f"causal MQA prefill, batch 0 of {shape['B']} ({shape['Hq']} heads x T={shape['T']} "
-                      f"x d={shape['D']}), fp64 numpy, {dt:.1f} s"}
+                      f"x d={shape['D']}), fp64 numpy, {reps} passes in {dt:.1f} s"}
 
 
 def copy_calibration(mib, reps):

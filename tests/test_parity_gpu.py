@@ -269,3 +269,63 @@ def test_mla_full_size(torch, mqa):
         ref, ref_lse = oracle.mla_absorbed_ref(round_bf16(qs)[None], round_bf16(kvs)[None], np.array([L]), scale)
         assert _maxerr(host(out[b]), ref[0]) <= BF16_TOL
         assert _maxerr(host(lse[b]), ref_lse[0]) <= BF16_TOL
+
+
+# ---------------------------------------------------------------------------
+# Running-maximum stress: key magnitudes grow along the sequence, so the
+# row maxima keep rising by far more than the kernels' lazy-rescale slack
+# (2^8) from tile to tile and every rescale path is taken many times.
+# ---------------------------------------------------------------------------
+
+def _grow_keys(t, axis, rate, cols=slice(None)):
+    """bf16 Tensor with slice j along `axis` (last-axis columns `cols` only)
+    multiplied by (1 + rate * j)."""
+    from synthetic import Tensor, bf16_bits
+    x = t.f32().copy()
+    shape = [1] * x.ndim
+    shape[axis] = x.shape[axis]
+    x[..., cols] *= (1.0 + rate * np.arange(x.shape[axis], dtype=np.float32)).reshape(shape)
+    return Tensor(bf16_bits(x), "bf16")
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,D", [(1, 16, 1, 300, 512), (1, 64, 8, 300, 128)])
+def test_prefill_growing_scores(torch, mqa, B, Hq, Hkv, T, D):
+    _say(f"prefill growing scores B{B} Hq{Hq} Hkv{Hkv} T{T} D{D}")
+    q, k, v = prefill_inputs(B, Hq, Hkv, T, D, "bf16", seed=7)
+    k = _grow_keys(k, 2, 0.1)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device="cuda")
+    out = mqa.mqa_prefill(dev(torch, q), dev(torch, k), dev(torch, v), causal=True, lse=lse)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.prefill_ref(q.f32(), k.f32(), v.f32(), 1 / math.sqrt(D), True)
+    assert np.all(np.isfinite(host(out)))
+    assert _maxerr(host(out), ref) <= BF16_TOL
+    assert _maxerr(host(lse), ref_lse) <= BF16_TOL
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,L,D,lengths", [(2, 16, 1, 2500, 512, [2500, 700]),
+                                                   (2, 64, 8, 2500, 128, [2500, 1300])])
+def test_decode_growing_scores(torch, mqa, B, Hq, Hkv, L, D, lengths):
+    _say(f"decode growing scores B{B} Hq{Hq} Hkv{Hkv} L{L} D{D}")
+    q, kc, vc, sl = decode_inputs(B, Hq, Hkv, L, D, "bf16", seed=8, lengths=lengths)
+    kc = _grow_keys(kc, 2, 0.02)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    out = mqa.mqa_decode(dev(torch, q), dev(torch, kc), dev(torch, vc), torch.from_numpy(sl).cuda(), lse=lse)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.decode_ref(q.f32(), kc.f32(), vc.f32(), sl, 1 / math.sqrt(D))
+    assert np.all(np.isfinite(host(out)))
+    assert _maxerr(host(out), ref) <= BF16_TOL
+    assert _maxerr(host(lse), ref_lse) <= BF16_TOL
+
+
+def test_mla_growing_scores(torch, mqa):
+    _say("mla growing scores B2 H128 L1500")
+    q, kv, sl = mla_inputs(2, 128, 1500, 576, "bf16", seed=9, lengths=[1500, 640])
+    # the latent is also the value: grow only the RoPE part (key-only columns)
+    kv = _grow_keys(kv, 1, 0.05, cols=slice(512, 576))
+    lse = torch.empty((2, 128), dtype=torch.float32, device="cuda")
+    out = mqa.mla_decode_absorbed(dev(torch, q), dev(torch, kv), torch.from_numpy(sl).cuda(), lse=lse)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.mla_absorbed_ref(q.f32(), kv.f32(), sl, 1 / math.sqrt(192))
+    assert np.all(np.isfinite(host(out)))
+    assert _maxerr(host(out), ref) <= BF16_TOL
+    assert _maxerr(host(lse), ref_lse) <= BF16_TOL
