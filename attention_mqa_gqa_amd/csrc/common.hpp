@@ -13,6 +13,9 @@
 // contraction pairs A slot j of group g with B slot j of group g.
 #pragma once
 
+#include <type_traits>
+#include <utility>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -251,6 +254,16 @@ __device__ __forceinline__ void sched_reads_ahead() {
     }
 }
 
+
+// Compile-time loop: f(std::integral_constant<int, 0>{}) ... up to N - 1.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
