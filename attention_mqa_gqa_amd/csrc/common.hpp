@@ -194,6 +194,22 @@ __device__ __forceinline__ void copy16_to_lds_async(const void* base, uint32_t v
         : "memory", "m0");
 }
 
+// Four consecutive 1 KB copies (global base + 1024 k -> LDS lds_byte +
+// 1024 k, k = 0..3) under one M0 write: the instruction offset moves both
+// the global and the LDS address.
+__device__ __forceinline__ void copy4x1k_to_lds_async(const void* base, uint32_t voff, uint32_t lds_byte) {
+    asm volatile(
+        "s_nop 4\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %0, %1\n\t"
+        "global_load_lds_dwordx4 %0, %1 offset:1024\n\t"
+        "global_load_lds_dwordx4 %0, %1 offset:2048\n\t"
+        "global_load_lds_dwordx4 %0, %1 offset:3072"
+        :
+        : "v"(voff), "s"(base), "s"(lds_byte)
+        : "memory", "m0");
+}
+
 // The same copy with the non-temporal hint, for data read exactly once
 // (an MLA latent cache streamed through LDS).
 __device__ __forceinline__ void copy16_to_lds_async_stream(const void* base, uint32_t voff, uint32_t lds_byte) {

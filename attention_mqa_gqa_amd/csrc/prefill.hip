@@ -187,10 +187,20 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     auto issue_v = [&](int tile) {
         const bf16* src = KVbh + (size_t)tile * 2 * TILE + TILE;
         const uint32_t dst = lds_base + (uint32_t)(2 * KSTAGE_B + (tile & 1) * VSTAGE_B);
+        if constexpr (LH % 4 == 0) {
+            // V^T tiles are contiguous in both places: each wave copies runs of
+            // 4 KB, four copies per M0 write
 #pragma unroll
-        for (int i = 0; i < LH; ++i) {
-            const int inst = i * NW + w;
-            copy16_to_lds_async(src + inst * 64 * 8, lane16, dst + (uint32_t)inst * 1024u);
+            for (int g = 0; g < LH / 4; ++g) {
+                const int inst = (g * NW + w) * 4;
+                copy4x1k_to_lds_async(src + inst * 64 * 8, lane16, dst + (uint32_t)inst * 1024u);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < LH; ++i) {
+                const int inst = i * NW + w;
+                copy16_to_lds_async(src + inst * 64 * 8, lane16, dst + (uint32_t)inst * 1024u);
+            }
         }
     };
 
@@ -565,7 +575,7 @@ PrefillPlan prefill_plan(int head_dim, int in_bf16) {
     PrefillPlan p{};
     if (!in_bf16) { p.rows_per_wg = 1 << 30; p.kt = 0; return p; }
     if (head_dim == 512) { p.rows_per_wg = 4 * 32 * 1; p.kt = 32; }
-    else if (head_dim == 128) { p.rows_per_wg = 4 * 32 * 2; p.kt = 32; }
+    else if (head_dim == 128) { p.rows_per_wg = 8 * 32 * 1; p.kt = 32; }
     return p;
 }
 
@@ -584,7 +594,9 @@ hipError_t prefill_launch(const PrefillArgs& a) {
         }
     }
     if (a.D == 512) return launch_bf16<512, 1, 4, 32>(a);
-    if (a.D == 128) return launch_bf16<128, 2, 4, 32>(a);
+    // d = 128: eight waves of one 32-row tile each (192 registers, two
+    // waves per SIMD, so one wave's softmax overlaps the other's MFMAs)
+    if (a.D == 128) return launch_bf16<128, 1, 8, 32>(a);
     return hipErrorInvalidValue;
 }
 
