@@ -82,9 +82,16 @@ def prefill_ref(q, k, v, scale, causal):
     """Full-sequence attention for MHA / GQA / MQA (prefill).
 
     q [B, Hq, T, dk]; k [B, Hkv, S, dk]; v [B, Hkv, S, dv]; Hq % Hkv == 0.
-    causal: key j is visible to query i iff j <= i (requires T == S; this is
-    the square lower-triangular mask of lzwjava §1 and of PyTorch SDPA's
-    ``is_causal=True`` used by the zdabc.icu benchmark section).
+    dk and dv may differ (the expanded MLA prefill of makesence §4.4 runs as
+    MHA with a 192-wide query/key and a 128-wide value, walkerchi §四 4.2).
+    causal: the T queries are the last T tokens of the S-token sequence, so
+    query i sits at position S - T + i and key j is visible to it iff
+    j <= S - T + i.  For T == S this is the square lower-triangular mask of
+    lzwjava §1 (and of SDPA's ``is_causal=True`` in the zdabc.icu benchmark
+    section); T < S is a block of new tokens after S - T earlier ones
+    (chunked prefill, or several decode tokens at once -- the pages only
+    show the square case, so this bottom-right alignment is a reading);
+    T > S is rejected, since a query row would see no key.
     Returns (out [B, Hq, T, dv], lse [B, Hq, T]).
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
@@ -92,13 +99,13 @@ def prefill_ref(q, k, v, scale, causal):
     Hkv, S = k.shape[1], k.shape[2]
     if Hq % Hkv:
         raise ValueError("Hq must be a multiple of Hkv")
-    if causal and T != S:
-        raise ValueError("causal prefill is defined here for T == S only")
+    if causal and T > S:
+        raise ValueError("causal prefill needs T <= S (every query must see a key)")
     n_rep = Hq // Hkv
     k_rep = repeat_kv_heads(k, n_rep)
     v_rep = repeat_kv_heads(v, n_rep)
     if causal:
-        visible = np.tril(np.ones((T, S), dtype=bool))
+        visible = np.tril(np.ones((T, S), dtype=bool), k=S - T)
     else:
         visible = np.ones((T, S), dtype=bool)
     out = np.empty((B, Hq, T, v.shape[-1]))
@@ -114,12 +121,15 @@ def prefill_rows_ref(q, k, v, rows, scale, causal):
     listed query rows ``rows = [(b, h, i), ...]`` (used to check full-size
     outputs on a sample).  Returns (out [n, dv], lse [n])."""
     Hq, Hkv = q.shape[1], k.shape[1]
+    T, S = q.shape[2], k.shape[2]
+    if causal and T > S:
+        raise ValueError("causal prefill needs T <= S (every query must see a key)")
     n_rep = Hq // Hkv
     out = np.empty((len(rows), v.shape[-1]))
     lse = np.empty(len(rows))
     for r, (b, h, i) in enumerate(rows):
         g = h // n_rep
-        last = i + 1 if causal else k.shape[2]
+        last = S - T + i + 1 if causal else S
         kk = _f64(k[b, g, :last])
         vv = _f64(v[b, g, :last])
         qq = _f64(q[b, h, i])[None, :]

@@ -119,13 +119,15 @@ def prefill_slice(seed, tid, b, H, T, D):
     return _draw(seed, tid, b, (H, T, D))
 
 
-def prefill_inputs(B, Hq, Hkv, T, D, dtype="bf16", seed=0, d_v=None):
-    """q [B,Hq,T,D], k [B,Hkv,T,D], v [B,Hkv,T,d_v], iid N(0,1)."""
+def prefill_inputs(B, Hq, Hkv, T, D, dtype="bf16", seed=0, d_v=None, T_kv=None):
+    """q [B,Hq,T,D], k [B,Hkv,T_kv,D], v [B,Hkv,T_kv,d_v], iid N(0,1)
+    (T_kv defaults to T, d_v to D)."""
     d_v = D if d_v is None else d_v
+    T_kv = T if T_kv is None else T_kv
     out = []
-    for tid, (H, dd) in enumerate(((Hq, D), (Hkv, D), (Hkv, d_v))):
-        t = _store((B, H, T, dd), dtype)
-        _parallel(lambda b: _put(t, b, _draw(seed, tid, b, (H, T, dd)), dtype), range(B))
+    for tid, (H, TT, dd) in enumerate(((Hq, T, D), (Hkv, T_kv, D), (Hkv, T_kv, d_v))):
+        t = _store((B, H, TT, dd), dtype)
+        _parallel(lambda b: _put(t, b, _draw(seed, tid, b, (H, TT, dd)), dtype), range(B))
         out.append(Tensor(t, dtype))
     return tuple(out)
 

@@ -80,6 +80,111 @@ def test_o1_prefill_rows_match_full():
         assert abs(l[r] - lse[b, h, i]) <= 1e-13
 
 
+def _brute_prefill_positions(q, k, v, scale, q_pos):
+    """Brute force with explicit token positions: query row i is the token at
+    position q_pos[i] and sees the keys at positions 0..q_pos[i]; q_pos None
+    means every key.  Pure Python arithmetic, as in _brute_row."""
+    B, Hq, T, _ = q.shape
+    Hkv, S = k.shape[1], k.shape[2]
+    grp = Hq // Hkv
+    out = np.zeros((B, Hq, T, v.shape[-1]))
+    lse = np.zeros((B, Hq, T))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // grp
+            for i in range(T):
+                seen = [j for j in range(S) if q_pos is None or j <= q_pos[i]]
+                keys = [list(map(float, k[b, g, j])) for j in seen]
+                vals = [list(map(float, v[b, g, j])) for j in seen]
+                o, s_ = _brute_row(list(map(float, q[b, h, i])), keys, vals, scale)
+                out[b, h, i], lse[b, h, i] = o, s_
+    return out, lse
+
+
+@pytest.mark.parametrize("T,S", [(3, 7), (1, 6), (5, 5), (4, 9)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_o1_chunk_prefill_brute_force(T, S, causal):
+    """T new tokens after S - T earlier ones: the queries are the LAST T
+    tokens of the sequence (token ids taken from the tail of range(S)); the
+    query/key width differs from the value width."""
+    rng = np.random.default_rng(15)
+    B, Hq, Hkv, D, DV = 2, 4, 2, 3, 5
+    q = rng.standard_normal((B, Hq, T, D))
+    k = rng.standard_normal((B, Hkv, S, D))
+    v = rng.standard_normal((B, Hkv, S, DV))
+    q_pos = list(range(S))[S - T:] if causal else None
+    o_ref, l_ref = oracle.prefill_ref(q, k, v, 0.45, causal)
+    o_bf, l_bf = _brute_prefill_positions(q, k, v, 0.45, q_pos)
+    assert np.max(np.abs(o_ref - o_bf)) <= 1e-12
+    assert np.max(np.abs(l_ref - l_bf)) <= 1e-12
+    rows = [(0, 0, 0), (1, 3, T - 1), (0, 2, T // 2)]
+    o_r, l_r = oracle.prefill_rows_ref(q, k, v, rows, 0.45, causal)
+    for r, (b, h, i) in enumerate(rows):
+        assert np.max(np.abs(o_r[r] - o_bf[b, h, i])) <= 1e-12
+        assert abs(l_r[r] - l_bf[b, h, i]) <= 1e-12
+
+
+def test_chunk_rows_equal_square_rows():
+    """A chunk of the last T queries against all S keys equals the last T
+    rows of the square causal prefill over the S tokens (the chunk is the
+    tail of the same sequence).  Pins the direction of the alignment: a
+    top-left mask would give the chunk's first row one key instead of
+    S - T + 1."""
+    q, k, v = (t.f32().astype(np.float64) for t in prefill_inputs(2, 4, 2, 11, 6, "f32", seed=16))
+    full, lfull = oracle.prefill_ref(q, k, v, 0.3, True)
+    for T in (1, 4, 11):
+        part, lpart = oracle.prefill_ref(q[:, :, 11 - T:], k, v, 0.3, True)
+        assert np.max(np.abs(part - full[:, :, 11 - T:])) <= 1e-13
+        assert np.max(np.abs(lpart - lfull[:, :, 11 - T:])) <= 1e-13
+
+
+def test_single_token_chunk_is_decode():
+    """T = 1 causal is one decode step over the S cached tokens."""
+    q, k, v = (t.f32().astype(np.float64) for t in prefill_inputs(3, 4, 1, 1, 5, "f32", seed=17, d_v=7, T_kv=9))
+    o, l = oracle.prefill_ref(q, k, v, 0.5, True)
+    od, ld = oracle.decode_ref(q[:, :, 0], k, v, np.array([9, 9, 9]), 0.5)
+    assert np.max(np.abs(o[:, :, 0] - od)) <= 1e-13
+    assert np.max(np.abs(l[:, :, 0] - ld)) <= 1e-13
+
+
+def test_causal_chunk_longer_than_keys_rejected():
+    q, k, v = (t.f32() for t in prefill_inputs(1, 2, 1, 6, 4, "f32", seed=18, T_kv=5))
+    with pytest.raises(ValueError):
+        oracle.prefill_ref(q, k, v, 0.5, True)
+    with pytest.raises(ValueError):
+        oracle.prefill_rows_ref(q, k, v, [(0, 0, 0)], 0.5, True)
+    oracle.prefill_ref(q, k, v, 0.5, False)    # no mask: any T, S
+
+
+def test_mla_expanded_prefill_equals_absorbed():
+    """Expanded MLA prefill (makesence §4.4: MHA with per-head keys
+    K_h = [c_kv W_UK[h] | k_pe] of width d_nope + d_R and values
+    V_h = c_kv W_UV[h] of width d_v) gives at causal row t the absorbed
+    decode of token t over the first t + 1 latent rows followed by W_UV[h]
+    (lzwjava §3), itself pinned to the explicit form above."""
+    rng = np.random.default_rng(35)
+    B, H, T, dc, dn, dr, dv = 2, 4, 9, 16, 8, 4, 6
+    q_nope = rng.standard_normal((B, H, T, dn))
+    q_rope = rng.standard_normal((B, H, T, dr))
+    c_kv = rng.standard_normal((B, T, dc))
+    k_pe = rng.standard_normal((B, T, dr))
+    w_uk = rng.standard_normal((H, dc, dn)) / math.sqrt(dc)
+    w_uv = rng.standard_normal((H, dc, dv)) / math.sqrt(dc)
+    scale = 1.0 / math.sqrt(dn + dr)
+    K = np.stack([np.concatenate([c_kv @ w_uk[h], k_pe], -1) for h in range(H)], axis=1)
+    V = np.stack([c_kv @ w_uv[h] for h in range(H)], axis=1)
+    Q = np.concatenate([q_nope, q_rope], -1)
+    out, lse = oracle.prefill_ref(Q, K, V, scale, True)
+    assert out.shape == (B, H, T, dv)
+    latent = np.concatenate([c_kv, k_pe], -1)
+    for t in range(T):
+        q_abs = oracle.absorb_query(q_nope[:, :, t], q_rope[:, :, t], w_uk)
+        o_lat, l_abs = oracle.mla_absorbed_ref(q_abs, latent, np.full(B, t + 1), scale, d_v=dc)
+        o_t = np.stack([o_lat[:, h] @ w_uv[h] for h in range(H)], axis=1)
+        assert np.max(np.abs(o_t - out[:, :, t])) <= 1e-10
+        assert np.max(np.abs(l_abs - lse[:, :, t])) <= 1e-10
+
+
 def test_o1_decode_brute_force():
     rng = np.random.default_rng(13)
     B, Hq, Hkv, L, D = 3, 4, 2, 6, 3
