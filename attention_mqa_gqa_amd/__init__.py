@@ -5,6 +5,8 @@ the library's HIP kernels.  PyTorch provides device memory and the stream.
 The entry points carry the C ABI's names (see ``include/mqa_attn.h``):
 
 * :func:`mqa_prefill`          -- causal or full attention over a sequence;
+* :func:`mqa_prefill_ex`       -- the same with T_q != T_kv (bottom-right
+  causal) and d_v != d_qk (expanded MLA prefill);
 * :func:`mqa_decode`           -- one query token per sequence vs a KV cache;
 * :func:`mla_decode_absorbed`  -- absorbed MLA decode over a latent cache.
 
@@ -24,6 +26,8 @@ __all__ = [
     "lib",
     "mqa_prefill",
     "mqa_prefill_workspace_size",
+    "mqa_prefill_ex",
+    "mqa_prefill_ex_workspace_size",
     "mqa_decode",
     "mqa_decode_workspace_size",
     "mla_decode_absorbed",
@@ -45,6 +49,8 @@ EXPORTED_SYMBOLS = (
     "mqa_last_hip_error_name",
     "mqa_prefill_workspace_size",
     "mqa_prefill",
+    "mqa_prefill_ex_workspace_size",
+    "mqa_prefill_ex",
     "mqa_decode_workspace_size",
     "mqa_decode",
     "mla_decode_workspace_size",
@@ -81,6 +87,10 @@ def _load():
     l.mqa_prefill_workspace_size.argtypes = [i, i, i, i, i, i]
     l.mqa_prefill.restype = i
     l.mqa_prefill.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, sz, vp]
+    l.mqa_prefill_ex_workspace_size.restype = sz
+    l.mqa_prefill_ex_workspace_size.argtypes = [i, i, i, i, i, i, i, i]
+    l.mqa_prefill_ex.restype = i
+    l.mqa_prefill_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, i, vp, sz, vp]
     l.mqa_decode_workspace_size.restype = sz
     l.mqa_decode_workspace_size.argtypes = [i, i, i, i, i]
     l.mqa_decode.restype = i
@@ -141,6 +151,10 @@ def mqa_prefill_workspace_size(B, Hq, Hkv, T, head_dim, in_dtype):
     return int(lib.mqa_prefill_workspace_size(B, Hq, Hkv, T, head_dim, in_dtype))
 
 
+def mqa_prefill_ex_workspace_size(B, Hq, Hkv, T_q, T_kv, d_qk, d_v, in_dtype):
+    return int(lib.mqa_prefill_ex_workspace_size(B, Hq, Hkv, T_q, T_kv, d_qk, d_v, in_dtype))
+
+
 def mqa_decode_workspace_size(B, Hq, Hkv, max_len, head_dim):
     return int(lib.mqa_decode_workspace_size(B, Hq, Hkv, max_len, head_dim))
 
@@ -184,6 +198,38 @@ def mqa_prefill(q, k, v, causal=True, scale=None, out=None, out_dtype=None, lse=
                          1 if causal else 0, in_code, _dtype_code(out.dtype), _ptr(ws), wsb,
                          _stream_ptr(stream, q.device))
     _check(st, "mqa_prefill")
+    return out
+
+
+def mqa_prefill_ex(q, k, v, causal=True, scale=None, out=None, out_dtype=None, lse=None,
+                   workspace=None, stream=None):
+    """q [B,Hq,T_q,d_qk], k [B,Hkv,T_kv,d_qk], v [B,Hkv,T_kv,d_v] ->
+    out [B,Hq,T_q,d_v] (and lse [B,Hq,T_q] if given).  causal: the queries
+    are the last T_q of the T_kv tokens.  Default scale 1/sqrt(d_qk)."""
+    torch = _torch()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, nm, 4)
+    B, Hq, T_q, DK = q.shape
+    Hkv, T_kv = k.shape[1], k.shape[2]
+    DV = v.shape[3]
+    if k.shape != (B, Hkv, T_kv, DK) or v.shape != (B, Hkv, T_kv, DV):
+        raise ValueError("k must be [B, Hkv, T_kv, d_qk] and v [B, Hkv, T_kv, d_v]")
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise TypeError("q, k, v must share a dtype")
+    in_code = _dtype_code(q.dtype)
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, Hq, T_q, DV), dtype=out_dtype, device=q.device)
+    _require(out, "out", 4)
+    if lse is not None:
+        _require(lse, "lse", 3)
+    scale = 1.0 / math.sqrt(DK) if scale is None else float(scale)
+    nbytes = mqa_prefill_ex_workspace_size(B, Hq, Hkv, T_q, T_kv, DK, DV, in_code)
+    ws, wsb = _workspace(nbytes, q.device, workspace)
+    st = lib.mqa_prefill_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, T_q, T_kv, DK, DV,
+                            scale, 1 if causal else 0, in_code, _dtype_code(out.dtype), _ptr(ws), wsb,
+                            _stream_ptr(stream, q.device))
+    _check(st, "mqa_prefill_ex")
     return out
 
 

@@ -29,10 +29,10 @@ int hip_status(hipError_t e) {
     return e == hipSuccess ? MQA_OK : MQA_ERR_HIP;
 }
 
-// bf16 prefill: rows per workgroup must hold at least one full head group.
-bool prefill_bf16_supported(int head_dim, int G) {
-    if (head_dim != 128 && head_dim != 512) return false;
-    const mqa::PrefillPlan p = mqa::prefill_plan(head_dim, 1);
+// Prefill widths / group size the kernels cover (bf16: rows per workgroup
+// must hold at least one full head group).
+bool prefill_supported(int d_qk, int d_v, int G, bool bf) {
+    const mqa::PrefillPlan p = mqa::prefill_plan(d_qk, d_v, bf ? 1 : 0);
     return G >= 1 && G <= p.rows_per_wg;
 }
 
@@ -59,48 +59,61 @@ const char* mqa_status_string(int status) {
     }
 }
 
-size_t mqa_prefill_workspace_size(int B, int Hq, int Hkv, int T, int head_dim, int in_dtype) {
+size_t mqa_prefill_ex_workspace_size(int B, int Hq, int Hkv, int T_q, int T_kv, int d_qk, int d_v, int in_dtype) {
     (void)Hq;
-    if (in_dtype != MQA_DTYPE_BF16 || B <= 0 || Hkv <= 0 || T <= 0 || head_dim <= 0) return 0;
-    const mqa::PrefillPlan p = mqa::prefill_plan(head_dim, 1);
+    (void)T_q;
+    if (in_dtype != MQA_DTYPE_BF16 || B <= 0 || Hkv <= 0 || T_kv <= 0 || d_qk <= 0 || d_v <= 0) return 0;
+    const mqa::PrefillPlan p = mqa::prefill_plan(d_qk, d_v, 1);
     if (p.kt <= 0) return 0;
-    const size_t tiles = ((size_t)T + p.kt - 1) / p.kt;
-    return (size_t)B * Hkv * tiles * p.kt * head_dim * 2 * 2;   // K tile + V^T tile, bf16
+    const size_t tiles = ((size_t)T_kv + p.kt - 1) / p.kt;
+    return (size_t)B * Hkv * tiles * p.kt * ((size_t)d_qk + d_v) * 2;   // K tile + V^T tile, bf16
 }
 
-int mqa_prefill(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv, int T,
-                int head_dim, float scale, int causal, int in_dtype, int out_dtype, void* workspace,
-                size_t workspace_bytes, void* stream) {
-    if (B < 0 || Hq <= 0 || Hkv <= 0 || T < 0 || head_dim <= 0) return MQA_ERR_INVALID_ARG;
+size_t mqa_prefill_workspace_size(int B, int Hq, int Hkv, int T, int head_dim, int in_dtype) {
+    return mqa_prefill_ex_workspace_size(B, Hq, Hkv, T, T, head_dim, head_dim, in_dtype);
+}
+
+int mqa_prefill_ex(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv,
+                   int T_q, int T_kv, int d_qk, int d_v, float scale, int causal, int in_dtype, int out_dtype,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || T_q < 0 || T_kv < 0 || d_qk <= 0 || d_v <= 0) return MQA_ERR_INVALID_ARG;
     if (Hq % Hkv != 0) return MQA_ERR_INVALID_ARG;
     if (!std::isfinite(scale) || !(scale > 0.f)) return MQA_ERR_INVALID_ARG;
     if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return MQA_ERR_INVALID_ARG;
-    if (B == 0 || T == 0) return MQA_OK;
+    // causal queries are the last T_q of T_kv tokens: more queries than keys
+    // would leave a query with no visible key
+    if (causal && T_q > T_kv) return MQA_ERR_INVALID_ARG;
+    if (B == 0 || T_q == 0) return MQA_OK;
+    if (T_kv == 0) return MQA_ERR_INVALID_ARG;   // queries with no key at all
     if (!q || !k || !v || !out) return MQA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || (lse && ((uintptr_t)lse & 3u)))
         return MQA_ERR_INVALID_ARG;
     const int G = Hq / Hkv;
     const bool bf = in_dtype == MQA_DTYPE_BF16;
-    if (bf) {
-        if (!prefill_bf16_supported(head_dim, G)) return MQA_ERR_UNSUPPORTED;
-    } else {
-        if (out_dtype != MQA_DTYPE_F32) return MQA_ERR_UNSUPPORTED;
-        if (head_dim % 64 != 0 || head_dim > 512) return MQA_ERR_UNSUPPORTED;
-    }
-    // the kernels address one (batch, KV head) slice of K with 32-bit byte offsets
-    if (bf && (size_t)T * head_dim * 2 > 0xFFFFFFFFull) return MQA_ERR_UNSUPPORTED;
-    const size_t need = mqa_prefill_workspace_size(B, Hq, Hkv, T, head_dim, in_dtype);
+    if (!bf && out_dtype != MQA_DTYPE_F32) return MQA_ERR_UNSUPPORTED;
+    if (!prefill_supported(d_qk, d_v, G, bf)) return MQA_ERR_UNSUPPORTED;
+    // the bf16 kernels address one (batch, KV head) tile stream with 32-bit
+    // byte offsets
+    if (bf && ((size_t)T_kv + 31) * ((size_t)d_qk + d_v) * 2 > 0xFFFFFFFFull) return MQA_ERR_UNSUPPORTED;
+    const size_t need = mqa_prefill_ex_workspace_size(B, Hq, Hkv, T_q, T_kv, d_qk, d_v, in_dtype);
     if (need > 0) {
         if (!workspace || workspace_bytes < need) return MQA_ERR_WORKSPACE;
         if (!aligned16(workspace)) return MQA_ERR_INVALID_ARG;
     }
     mqa::PrefillArgs a;
     a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
-    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.T = T; a.D = head_dim; a.G = G;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Tq = T_q; a.Tkv = T_kv; a.DK = d_qk; a.DV = d_v; a.G = G;
     a.scale = scale; a.causal = causal != 0; a.in_bf16 = bf; a.out_f32 = out_dtype == MQA_DTYPE_F32;
     a.workspace = workspace; a.stream = (hipStream_t)stream;
     clear_stale_error();
     return hip_status(mqa::prefill_launch(a));
+}
+
+int mqa_prefill(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv, int T,
+                int head_dim, float scale, int causal, int in_dtype, int out_dtype, void* workspace,
+                size_t workspace_bytes, void* stream) {
+    return mqa_prefill_ex(q, k, v, out, lse, B, Hq, Hkv, T, T, head_dim, head_dim, scale, causal, in_dtype,
+                          out_dtype, workspace, workspace_bytes, stream);
 }
 
 size_t mqa_decode_workspace_size(int B, int Hq, int Hkv, int max_len, int head_dim) {

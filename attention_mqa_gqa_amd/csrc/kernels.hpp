@@ -14,7 +14,10 @@ struct PrefillArgs {
     const void* v;
     void* out;
     float* lse;
-    int B, Hq, Hkv, T, D, G;
+    int B, Hq, Hkv;
+    int Tq, Tkv;      // query tokens, key tokens (causal: Tq <= Tkv, bottom-right)
+    int DK, DV;       // query/key width, value width
+    int G;
     float scale;
     bool causal;
     bool in_bf16;
@@ -24,11 +27,11 @@ struct PrefillArgs {
 };
 
 struct PrefillPlan {
-    int rows_per_wg;  // query rows (heads x tokens) per workgroup, bf16 path
+    int rows_per_wg;  // query rows (heads x tokens) per workgroup; 0 = widths unsupported
     int kt;           // keys per K/V tile, bf16 path
 };
 
-PrefillPlan prefill_plan(int head_dim, int in_bf16);
+PrefillPlan prefill_plan(int d_qk, int d_v, int in_bf16);
 hipError_t prefill_launch(const PrefillArgs& a);
 
 // Split-KV decode plan shared by the workspace query and the launch.

@@ -70,9 +70,22 @@ MQA_HD constexpr int c32_index(int h, int i) { return 16 * (i >> 3) + 8 * h + (i
 MQA_HD constexpr int swz32_16(int r) { return swap23(r & 15); }
 MQA_HD constexpr int swz32_8(int r) { return ((r >> 1) & 1) | (((r >> 3) & 1) << 1) | (((r ^ (r >> 2)) & 1) << 2); }
 MQA_HD constexpr int swz32_4(int r) { return ((r >> 3) & 1) | ((((r >> 1) ^ (r >> 2)) & 1) << 1); }
+// Rows of an odd multiple of 8 chunks (24: a 192-wide bf16 row).  Row r
+// starts at chunk 24r, i.e. 8 (r & 1) modulo 16, so the row parity already
+// separates two halves of a 256-byte bank window; the swizzle permutes
+// chunks within aligned groups of 8 and must be one-to-one on the rows of
+// one parity (16-lane groups) and on the rows of one 8-lane group (rows
+// {0-3, 8-11} or {4-7, 12-15} after swap23).
+MQA_HD constexpr int swz32_x8(int r) { return ((r ^ (r >> 2)) & 1) | (r & 2) | (((r >> 3) & 1) << 2); }
 MQA_HD constexpr int swz32(int r, int row_chunks) {
-    return row_chunks >= 16 ? swz32_16(r) : (row_chunks == 8 ? swz32_8(r) : swz32_4(r));
+    return row_chunks % 16 == 0 ? swz32_16(r)
+         : row_chunks == 8      ? swz32_8(r)
+         : row_chunks % 16 == 8 ? swz32_x8(r)
+                                : swz32_4(r);
 }
+// chunks per swizzle group of a 32-row operand row (the swizzle keeps a
+// chunk inside its aligned group of this many chunks)
+MQA_HD constexpr int swz32_group(int row_chunks) { return row_chunks % 16 == 0 ? 16 : (row_chunks % 8 == 0 ? 8 : 4); }
 
 // Rows that are one 1 KB copy each (K rows at D = 512, MLA latent rows) are
 // stored with 16 bytes of padding, key row r at row position swap23(r): the

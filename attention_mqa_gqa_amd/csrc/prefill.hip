@@ -7,15 +7,18 @@
 //     ALL G query heads of that KV head, so every K/V tile staged in LDS is
 //     reused by the whole head group (the MQA/GQA saving; heads are indexed,
 //     never copied -- lzwjava §2);
-//   * per wave: 16*NT query rows; S^T = K Q^T and O^T += V^T P^T on
-//     v_mfma_f32_16x16x32_bf16 with fp32 accumulation; Q stays in VGPRs,
-//     the O^T accumulator for the full head dim stays in (A)VGPRs;
+//   * per wave: 32*NR query rows; S^T = K Q^T and O^T += V^T P^T on
+//     v_mfma_f32_32x32x16_bf16 with fp32 accumulation; Q stays in VGPRs,
+//     the O^T accumulator for the full value width stays in AGPRs;
 //   * online softmax per row in registers (exp2 domain, lazy rescale);
 //   * K tiles and pre-transposed V tiles are copied global->LDS with
 //     asynchronous direct-to-LDS loads, double buffered;
 //   * causal: key tiles past the block's last token are never visited, the
 //     diagonal tile is masked per element, and the heaviest blocks start
 //     first.
+// Queries and keys may differ in number (T_q <= T_kv when causal: the
+// queries are the last T_q tokens of the sequence) and the value width may
+// differ from the query/key width (expanded MLA prefill: 192 / 128).
 // fp32 path: a plain fp32 VALU kernel (no reduced-precision operands).
 #include <type_traits>
 
@@ -26,38 +29,40 @@
 namespace mqa {
 
 // ---------------------------------------------------------------------------
-// K, V [B*Hkv, T, D] -> tile stream [B*Hkv, n_tiles, (K tile | V^T tile)].
+// K [B*Hkv, T, DK], V [B*Hkv, T, DV] -> tile stream
+// [B*Hkv, n_tiles, (K tile | V^T tile)].
 // Each 32-key tile is stored as the prefill kernel keeps it in LDS: the K
 // tile row-major (row = key; 16-byte chunks in swizzled order unless a row
 // is exactly one 1 KB copy, which the kernel places with padding instead)
-// and the V^T tile (row = head dim, 32 keys per row, swizzled chunks), zero
+// and the V^T tile (row = value dim, 32 keys per row, swizzled chunks), zero
 // past T.  V's
 // contraction index (the key) is its row index, so the P.V operand needs it
 // transposed; doing that here once, and storing both tiles contiguously,
 // turns every global->LDS copy of the main kernel into a straight 16-byte
 // stream (uniform base + 16 * lane).
 // ---------------------------------------------------------------------------
-template <int D, int KT>
+template <int DK, int DV, int KT>
 __global__ __launch_bounds__(256) void kv_pack_kernel(const bf16* __restrict__ K, const bf16* __restrict__ V,
                                                       bf16* __restrict__ KVt, int T, int n_tiles) {
     constexpr int RL = KT / 8;           // 16-byte chunks per V^T row
-    constexpr int ROW_CHUNKS = D / 8;    // 16-byte chunks per K row
-    constexpr int NB = RL * (D / 8);     // 8x8 blocks per V tile
-    constexpr int TILE = KT * D;
+    constexpr int ROW_CHUNKS = DK / 8;   // 16-byte chunks per K row
+    constexpr int NB = RL * (DV / 8);    // 8x8 blocks per V tile
+    constexpr int TILE_K = KT * DK;
+    constexpr int TILE_V = KT * DV;
     const int tile = blockIdx.x;
     const size_t bh = blockIdx.y;
-    const bf16* ksrc = K + bh * (size_t)T * D;
-    const bf16* vsrc = V + bh * (size_t)T * D;
-    bf16* kdst = KVt + (bh * n_tiles + tile) * (size_t)(2 * TILE);
-    bf16* vdst = kdst + TILE;
+    const bf16* ksrc = K + bh * (size_t)T * DK;
+    const bf16* vsrc = V + bh * (size_t)T * DV;
+    bf16* kdst = KVt + (bh * n_tiles + tile) * (size_t)(TILE_K + TILE_V);
+    bf16* vdst = kdst + TILE_K;
     // K tile: chunk position p of row kk holds global chunk p ^ swz(kk)
     // (plain order for 1 KB rows)
     for (int q = threadIdx.x; q < KT * ROW_CHUNKS; q += 256) {
         const int kk = q / ROW_CHUNKS;
         const int p = q % ROW_CHUNKS;
-        const int c = (2 * D == 1024) ? p : (p ^ layout::swz32(kk, ROW_CHUNKS));
+        const int c = (2 * DK == 1024) ? p : (p ^ layout::swz32(kk, ROW_CHUNKS));
         const int key = tile * KT + kk;
-        const u32x4 val = key < T ? ldg16(ksrc + (size_t)key * D + c * 8) : u32x4{0, 0, 0, 0};
+        const u32x4 val = key < T ? ldg16(ksrc + (size_t)key * DK + c * 8) : u32x4{0, 0, 0, 0};
         *(u32x4*)(kdst + (size_t)q * 8) = val;
     }
     // V^T tile: 8x8 blocks transposed with byte permutes
@@ -68,7 +73,7 @@ __global__ __launch_bounds__(256) void kv_pack_kernel(const bf16* __restrict__ K
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int key = tile * KT + kb * 8 + j;
-            if (key < T) r[j] = ldg16(vsrc + (size_t)key * D + db * 8);
+            if (key < T) r[j] = ldg16(vsrc + (size_t)key * DV + db * 8);
             else r[j] = u32x4{0, 0, 0, 0};
         }
 #pragma unroll
@@ -89,39 +94,51 @@ __global__ __launch_bounds__(256) void kv_pack_kernel(const bf16* __restrict__ K
 
 // ---------------------------------------------------------------------------
 // bf16 flash prefill on v_mfma_f32_32x32x16_bf16.
-//   D   head dim (128 or 512)        NR  32-row N-tiles per wave
-//   NW  waves per workgroup          KT  keys per tile (32)
-// Each wave owns 32*NR query rows with the full head dim: Q^T operands and
+//   DK  query/key width (128, 192 or 512)   DV  value width (128 or 512)
+//   NR  32-row N-tiles per wave             NW  waves per workgroup
+//   KT  keys per tile (32)
+// Each wave owns 32*NR query rows with the full widths: Q^T operands and
 // the O^T accumulator stay in registers for the whole key loop (one wave per
-// SIMD at D = 512).  Rows of a workgroup: r = 0 .. NW*32*NR-1, head = r % G,
+// SIMD at 512).  Rows of a workgroup: r = 0 .. NW*32*NR-1, head = r % G,
 // token = t0 + r / G.  Keys inside a tile follow layout::swap23 so that the
 // score accumulators are the P operands of the P.V MFMA as they stand.
+// Causal: query token i (of Tq) sees keys j <= i + q_off, q_off = Tkv - Tq.
 // ---------------------------------------------------------------------------
-template <int D, int NR, int NW, int KT, bool CAUSAL, bool OUT_F32>
+template <int DK, int DV, int NR, int NW, int KT, bool CAUSAL, bool OUT_F32>
 __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ KVt,
-    void* __restrict__ Out, float* __restrict__ Lse, int Hq, int Hkv, int T, int G,
-    int tok_per_wg, int n_tok_blocks, int n_kv_tiles, float scale_log2) {
+    void* __restrict__ Out, float* __restrict__ Lse, int Hq, int Hkv, int Tq, int Tkv, int q_off,
+    int G, int tok_per_wg, int n_tok_blocks, int n_kv_tiles, float scale_log2) {
     constexpr int RW = 32 * NR;           // rows per wave
-    constexpr int KS = D / 16;            // QK^T contraction steps
-    constexpr int MT_O = D / 32;          // O^T M-tiles (head dims)
+    constexpr int KS = DK / 16;           // QK^T contraction steps
+    constexpr int MT_O = DV / 32;         // O^T M-tiles (value dims)
     constexpr int KSP = KT / 16;          // P.V contraction steps
     constexpr int RL = KT / 8;            // chunks per V^T row
-    constexpr int TILE = KT * D;          // elements per K tile (and per V^T tile)
-    constexpr int LH = TILE / 8 / (NW * 64);   // 16-byte copies per thread per K (or V^T) tile
-    constexpr int ROW_CHUNKS = D / 8;
-    // K rows of 1 KB (D = 512) are one copy instruction each, so in LDS each
+    constexpr int TILE_K = KT * DK;       // elements per K tile
+    constexpr int TILE_V = KT * DV;       // elements per V^T tile
+    constexpr int ROW_CHUNKS = DK / 8;
+    // 1 KB copies per tile; a K tile that does not split evenly over the
+    // waves ends with one round in which every wave copies PLK lanes' worth
+    // (so every wave issues the same number of copy instructions)
+    constexpr int CK = TILE_K * 2 / 1024;
+    constexpr int CV = TILE_V * 2 / 1024;
+    constexpr int FK = CK / NW;                            // full K copy rounds
+    constexpr int PLK = (CK % NW) * 64 / NW;               // lanes per wave in the last round
+    constexpr int LHK = FK + (PLK ? 1 : 0);                // copy instructions per wave per K tile
+    constexpr int LHV = CV / NW;                           // ... per V^T tile
+    // K rows of 1 KB (DK = 512) are one copy instruction each, so in LDS each
     // row can start 16 bytes after the previous one ends (and rows can be
     // placed in any order): the 8 or 16 lanes served together then read
     // distinct bank slots without any swizzle, and a lane reads every
     // contraction step of its row from one address register plus an
     // immediate offset.  Narrower rows are swizzled instead.
-    constexpr bool KPAD = (2 * D == 1024);
-    constexpr int KROW_B = KPAD ? layout::padded_row_bytes(2 * D) : 2 * D;   // LDS bytes per K row
+    constexpr bool KPAD = (2 * DK == 1024);
+    constexpr int KROW_B = KPAD ? layout::padded_row_bytes(2 * DK) : 2 * DK;   // LDS bytes per K row
     constexpr int KSTAGE_B = KT * KROW_B;                  // LDS bytes per K stage
-    constexpr int VSTAGE_B = 2 * TILE;                     // LDS bytes per V^T stage
+    constexpr int VSTAGE_B = 2 * TILE_V;                   // LDS bytes per V^T stage
     static_assert(KT == 32, "key tile");
-    static_assert((TILE / 8) % (NW * 64) == 0, "tile must split evenly over the waves");
+    static_assert(CV % NW == 0, "V^T tile must split evenly over the waves");
+    static_assert((CK % NW) * 64 % NW == 0 && (!KPAD || PLK == 0), "K tile split");
 
     __shared__ __attribute__((aligned(16))) char smem[2 * KSTAGE_B + 2 * VSTAGE_B];
 
@@ -134,6 +151,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     const int b = blockIdx.z;
     const int t0 = tb * tok_per_wg;
     const int rows_used = tok_per_wg * G;
+    (void)n_tok_blocks;
 
     int row_tok[NR];
     int row_head[NR];
@@ -143,14 +161,14 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
         const int r = w * RW + 32 * nt + n;
         row_tok[nt] = t0 + r / G;
         row_head[nt] = hk * G + r % G;
-        row_ok[nt] = (r < rows_used) && (row_tok[nt] < T);
+        row_ok[nt] = (r < rows_used) && (row_tok[nt] < Tq);
     }
 
     // Q^T operands: lane half h2 holds head dims 16ks + 8h2 .. +7 of row n.
     bf16x8 qb[NR][KS];
 #pragma unroll
     for (int nt = 0; nt < NR; ++nt) {
-        const bf16* qrow = Q + (((size_t)b * Hq + row_head[nt]) * T + (row_ok[nt] ? row_tok[nt] : 0)) * D;
+        const bf16* qrow = Q + (((size_t)b * Hq + row_head[nt]) * Tq + (row_ok[nt] ? row_tok[nt] : 0)) * DK;
         const u32x4 zero = {0, 0, 0, 0};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -160,10 +178,10 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     }
 
     const size_t bh = (size_t)b * Hkv + hk;
-    const bf16* KVbh = KVt + bh * (size_t)n_kv_tiles * 2 * TILE;
+    const bf16* KVbh = KVt + bh * (size_t)n_kv_tiles * (TILE_K + TILE_V);
 
-    const int t_last = min(T, t0 + tok_per_wg) - 1;
-    const int n_tiles = CAUSAL ? (t_last / KT + 1) : n_kv_tiles;
+    const int t_last = min(Tq, t0 + tok_per_wg) - 1;
+    const int n_tiles = CAUSAL ? ((t_last + q_off) / KT + 1) : n_kv_tiles;
 
     // LDS: K stages 0/1, then V^T stages 0/1; tile j lives in stage j & 1.
     // Iteration t computes S(t+1) next to softmax(t) (between barriers A and
@@ -175,29 +193,35 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     const uint32_t lds_base = lds_addr(smem);
     const uint32_t lane16 = (uint32_t)lane * 16u;
     auto issue_k = [&](int tile) {
-        const bf16* src = KVbh + (size_t)tile * 2 * TILE;
+        const bf16* src = KVbh + (size_t)tile * (TILE_K + TILE_V);
         const uint32_t dst = lds_base + (uint32_t)((tile & 1) * KSTAGE_B);
 #pragma unroll
-        for (int i = 0; i < LH; ++i) {
+        for (int i = 0; i < FK; ++i) {
             const int inst = i * NW + w;               // wave-uniform
             const uint32_t pos = KPAD ? (uint32_t)layout::padded_row_pos(inst) * KROW_B : (uint32_t)inst * 1024u;
             copy16_to_lds_async(src + inst * 64 * 8, lane16, dst + pos);
         }
+        if constexpr (PLK != 0) {
+            // last round: wave w copies bytes [FK NW 1 KB + 16 PLK w, +16 PLK)
+            // of the (unpadded) tile with its first PLK lanes
+            const uint32_t off = (uint32_t)(FK * NW * 1024 + w * PLK * 16);
+            if (lane < PLK) copy16_to_lds_async((const char*)src + off, lane16, dst + off);
+        }
     };
     auto issue_v = [&](int tile) {
-        const bf16* src = KVbh + (size_t)tile * 2 * TILE + TILE;
+        const bf16* src = KVbh + (size_t)tile * (TILE_K + TILE_V) + TILE_K;
         const uint32_t dst = lds_base + (uint32_t)(2 * KSTAGE_B + (tile & 1) * VSTAGE_B);
-        if constexpr (LH % 4 == 0) {
+        if constexpr (LHV % 4 == 0) {
             // V^T tiles are contiguous in both places: each wave copies runs of
             // 4 KB, four copies per M0 write
 #pragma unroll
-            for (int g = 0; g < LH / 4; ++g) {
+            for (int g = 0; g < LHV / 4; ++g) {
                 const int inst = (g * NW + w) * 4;
                 copy4x1k_to_lds_async(src + inst * 64 * 8, lane16, dst + (uint32_t)inst * 1024u);
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < LH; ++i) {
+            for (int i = 0; i < LHV; ++i) {
                 const int inst = i * NW + w;
                 copy16_to_lds_async(src + inst * 64 * 8, lane16, dst + (uint32_t)inst * 1024u);
             }
@@ -214,21 +238,24 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     for (int nt = 0; nt < NR; ++nt) { m_run[nt] = -INFINITY; l_run[nt] = 0.f; }
 
     // K operand of contraction step ks for this lane (key row swap23(n),
-    // head dims 16ks + 8h2 .. +7), as a byte offset into a K stage.  Padded
-    // rows: one base plus 32 ks.  Swizzled rows: the swizzle only permutes
-    // chunks within aligned groups of 16, so 8 lane offsets plus an
-    // immediate stride of 256 bytes per 8 steps cover every step.
+    // dims 16ks + 8h2 .. +7), as a byte offset into a K stage.  Padded rows:
+    // one base plus 32 ks.  Swizzled rows: the swizzle only permutes chunks
+    // within aligned groups of GS (16, or 8 for 24-chunk rows), so GS/2 lane
+    // offsets plus an immediate stride of 16 GS bytes per GS/2 steps cover
+    // every step.
     const int krow = layout::swap23(n);
     const uint32_t kpad_off = (uint32_t)(n * KROW_B + h2 * 16);
-    uint32_t koff[KPAD ? 1 : 8];
+    constexpr int GS = layout::swz32_group(ROW_CHUNKS);
+    constexpr int NKO = GS / 2;
+    uint32_t koff[KPAD ? 1 : NKO];
     if constexpr (!KPAD) {
         const int k_swz = layout::swz32(krow, ROW_CHUNKS);
 #pragma unroll
-        for (int v = 0; v < 8; ++v) koff[v] = (uint32_t)(krow * 2 * D + (((2 * v + h2) ^ k_swz) * 16));
+        for (int v = 0; v < NKO; ++v) koff[v] = (uint32_t)(krow * 2 * DK + (((2 * v + h2) ^ k_swz) * 16));
     }
     auto kread = [&](const char* kst, int ks) {
         if constexpr (KPAD) return *(const bf16x8*)(kst + kpad_off + ks * 32);
-        else return *(const bf16x8*)(kst + koff[ks & 7] + (ks >> 3) * 256);
+        else return *(const bf16x8*)(kst + koff[ks % NKO] + (ks / NKO) * (GS * 16));
     };
     constexpr int PF = 4;
 
@@ -254,7 +281,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
         const int j0 = tile * KT;
 #pragma unroll
         for (int nt = 0; nt < NR; ++nt) {
-            const int lim = (CAUSAL ? min(row_tok[nt], T - 1) : T - 1) - j0;
+            const int lim = (CAUSAL ? min(row_tok[nt] + q_off, Tkv - 1) : Tkv - 1) - j0;
 #pragma unroll
             for (int i = 0; i < 16; ++i)
                 if (layout::c32_index(h2, i) > lim) sc[nt][i] = -INFINITY;
@@ -264,7 +291,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     const int wave_tok_min = t0 + (w * RW) / G;
     auto tile_masked = [&](int tile) {
         const int last_key = tile * KT + KT - 1;
-        return last_key >= T || (CAUSAL && last_key > wave_tok_min);
+        return last_key >= Tkv || (CAUSAL && last_key > wave_tok_min + q_off);
     };
     const float c = scale_log2;
 
@@ -273,7 +300,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     issue_k(0);
     if (n_tiles > 1) issue_k(1);
     issue_v(0);
-    wait_vmcnt_of<LH, LH>(n_tiles > 1 ? 2 * LH : LH);   // K(0) has landed
+    wait_vmcnt_of<LHK, LHV>(n_tiles > 1 ? LHK + LHV : LHV);   // K(0) has landed
     __syncthreads();
     f32x16 sA[NR], sB[NR];
 #pragma unroll
@@ -306,7 +333,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
         const bool has_next = it + 1 < n_tiles;
         const bool has_next2 = it + 2 < n_tiles;
         // K(it+1) has landed; V(it) and K(it+2) may still be in flight
-        if (has_next) wait_vmcnt_of<LH, LH>(LH + (has_next2 ? LH : 0));
+        if (has_next) wait_vmcnt_of<LHK, LHV>(LHV + (has_next2 ? LHK : 0));
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();                                       // barrier A
 
@@ -360,7 +387,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
         }
 
         // V(it) has landed (K(it+2) and V(it+1) may still be in flight)
-        wait_vmcnt_of<LH, LH>((has_next2 ? LH : 0) + (has_next ? LH : 0));
+        wait_vmcnt_of<LHK, LHV>((has_next2 ? LHK : 0) + (has_next ? LHV : 0));
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();                                       // barrier B
 
@@ -432,7 +459,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
         const float l = sum_over_halves(l_run[nt]);
         const float inv = 1.f / l;
         if (!row_ok[nt]) continue;
-        const size_t row = ((size_t)b * Hq + row_head[nt]) * T + row_tok[nt];
+        const size_t row = ((size_t)b * Hq + row_head[nt]) * Tq + row_tok[nt];
 #pragma unroll
         for (int mt = 0; mt < MT_O; ++mt) {
 #pragma unroll
@@ -442,11 +469,11 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
                 const f32x4 hi = f32x4{acc[8 * half + 4], acc[8 * half + 5], acc[8 * half + 6], acc[8 * half + 7]} * inv;
                 const int d0 = 32 * mt + layout::c32_index(h2, 8 * half);
                 if constexpr (OUT_F32) {
-                    float* dst = (float*)Out + row * D + d0;
+                    float* dst = (float*)Out + row * DV + d0;
                     *(f32x4*)dst = lo;
                     *(f32x4*)(dst + 4) = hi;
                 } else {
-                    bf16* dst = (bf16*)Out + row * D + d0;
+                    bf16* dst = (bf16*)Out + row * DV + d0;
                     *(bf16x8*)dst = pack_bf16x8(lo, hi);
                 }
             }
@@ -457,15 +484,17 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
 
 // ---------------------------------------------------------------------------
 // fp32 prefill: genuine fp32 end to end (fp32 FMA, fp32 exp2).  One wave
-// handles four consecutive query tokens of one head; lanes split the head
-// dim (E = D/64 consecutive elements per lane).  Online softmax per row.
+// handles four consecutive query tokens of one head; lanes split the widths
+// (DK/64 query/key and DV/64 value elements per lane).  Online softmax per
+// row.  Causal: query token i sees keys j <= i + q_off.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int DK, int DV, bool CAUSAL>
 __global__ __launch_bounds__(256) void prefill_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                           const float* __restrict__ V, float* __restrict__ Out,
-                                                          float* __restrict__ Lse, int Hq, int Hkv, int T, int G,
-                                                          float scale_log2) {
-    constexpr int E = D / 64;
+                                                          float* __restrict__ Lse, int Hq, int Hkv, int Tq, int Tkv,
+                                                          int q_off, int G, float scale_log2) {
+    constexpr int EK = DK / 64;
+    constexpr int EV = DV / 64;
     constexpr int RPW = 4;
     const int lane = lane_id();
     const int w = wave_id();
@@ -474,31 +503,35 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(const float* __restric
     const int hk = h / G;
     const int tb = CAUSAL ? ((int)gridDim.x - 1 - (int)blockIdx.x) : (int)blockIdx.x;
     const int tbase = tb * (4 * RPW) + w * RPW;
-    if (tbase >= T) return;
+    if (tbase >= Tq) return;
 
-    const float* Kbh = K + ((size_t)b * Hkv + hk) * (size_t)T * D;
-    const float* Vbh = V + ((size_t)b * Hkv + hk) * (size_t)T * D;
-    float q[RPW][E], o[RPW][E], m[RPW], l[RPW];
+    const float* Kbh = K + ((size_t)b * Hkv + hk) * (size_t)Tkv * DK;
+    const float* Vbh = V + ((size_t)b * Hkv + hk) * (size_t)Tkv * DV;
+    float q[RPW][EK], o[RPW][EV], m[RPW], l[RPW];
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
-        const int t = min(tbase + r, T - 1);
-        const float* qrow = Q + (((size_t)b * Hq + h) * T + t) * D + lane * E;
+        const int t = min(tbase + r, Tq - 1);
+        const float* qrow = Q + (((size_t)b * Hq + h) * Tq + t) * DK + lane * EK;
 #pragma unroll
-        for (int e = 0; e < E; ++e) { q[r][e] = qrow[e]; o[r][e] = 0.f; }
+        for (int e = 0; e < EK; ++e) q[r][e] = qrow[e];
+#pragma unroll
+        for (int e = 0; e < EV; ++e) o[r][e] = 0.f;
         m[r] = -INFINITY;
         l[r] = 0.f;
     }
-    const int jmax = CAUSAL ? min(tbase + RPW - 1, T - 1) : T - 1;
+    const int jmax = CAUSAL ? min(tbase + RPW - 1 + q_off, Tkv - 1) : Tkv - 1;
     for (int j = 0; j <= jmax; ++j) {
-        float kv[E], vv[E];
+        float kv[EK], vv[EV];
 #pragma unroll
-        for (int e = 0; e < E; ++e) { kv[e] = Kbh[(size_t)j * D + lane * E + e]; vv[e] = Vbh[(size_t)j * D + lane * E + e]; }
+        for (int e = 0; e < EK; ++e) kv[e] = Kbh[(size_t)j * DK + lane * EK + e];
+#pragma unroll
+        for (int e = 0; e < EV; ++e) vv[e] = Vbh[(size_t)j * DV + lane * EV + e];
         float dot[RPW];
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
             float acc = 0.f;
 #pragma unroll
-            for (int e = 0; e < E; ++e) acc = fmaf(q[r][e], kv[e], acc);
+            for (int e = 0; e < EK; ++e) acc = fmaf(q[r][e], kv[e], acc);
             dot[r] = acc;
         }
 #pragma unroll
@@ -507,25 +540,25 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(const float* __restric
             for (int r = 0; r < RPW; ++r) dot[r] += __shfl_xor(dot[r], off);
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
-            if (CAUSAL && j > tbase + r) continue;
+            if (CAUSAL && j > tbase + r + q_off) continue;
             const float sc = dot[r] * scale_log2;
             const float mnew = fmaxf(m[r], sc);
             const float alpha = fast_exp2(m[r] - mnew);
             const float p = fast_exp2(sc - mnew);
             l[r] = l[r] * alpha + p;
 #pragma unroll
-            for (int e = 0; e < E; ++e) o[r][e] = fmaf(p, vv[e], o[r][e] * alpha);
+            for (int e = 0; e < EV; ++e) o[r][e] = fmaf(p, vv[e], o[r][e] * alpha);
             m[r] = mnew;
         }
     }
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
         const int t = tbase + r;
-        if (t >= T) continue;
-        const size_t row = ((size_t)b * Hq + h) * T + t;
+        if (t >= Tq) continue;
+        const size_t row = ((size_t)b * Hq + h) * Tq + t;
         const float inv = 1.f / l[r];
 #pragma unroll
-        for (int e = 0; e < E; ++e) Out[row * D + lane * E + e] = o[r][e] * inv;
+        for (int e = 0; e < EV; ++e) Out[row * DV + lane * EV + e] = o[r][e] * inv;
         if (Lse != nullptr && lane == 0) Lse[row] = m[r] * kLn2 + logf(l[r]);
     }
 }
@@ -533,21 +566,22 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(const float* __restric
 // ---------------------------------------------------------------------------
 // Host-side launchers (validated arguments only).
 // ---------------------------------------------------------------------------
-template <int D, int NR, int NW, int KT>
+template <int DK, int DV, int NR, int NW, int KT>
 static hipError_t launch_bf16(const PrefillArgs& a) {
     const int R = NW * 32 * NR;
     const int tok = R / a.G;
-    const int n_tok_blocks = (a.T + tok - 1) / tok;
-    const int n_kv_tiles = (a.T + KT - 1) / KT;
+    const int n_tok_blocks = (a.Tq + tok - 1) / tok;
+    const int n_kv_tiles = (a.Tkv + KT - 1) / KT;
+    const int q_off = a.Tkv - a.Tq;
     bf16* kvt = (bf16*)a.workspace;
-    hipLaunchKernelGGL((kv_pack_kernel<D, KT>), dim3(n_kv_tiles, a.B * a.Hkv), dim3(256), 0, a.stream,
-                       (const bf16*)a.k, (const bf16*)a.v, kvt, a.T, n_kv_tiles);
+    hipLaunchKernelGGL((kv_pack_kernel<DK, DV, KT>), dim3(n_kv_tiles, a.B * a.Hkv), dim3(256), 0, a.stream,
+                       (const bf16*)a.k, (const bf16*)a.v, kvt, a.Tkv, n_kv_tiles);
     const dim3 grid(n_tok_blocks, a.Hkv, a.B);
     const float sl2 = a.scale * kLog2e;
-#define MQA_PREFILL_LAUNCH(C, F)                                                                      \
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, NR, NW, KT, C, F>), grid, dim3(NW * 64), 0, a.stream, \
-                       (const bf16*)a.q, (const bf16*)kvt, a.out, a.lse, a.Hq, a.Hkv, a.T, a.G, tok,      \
-                       n_tok_blocks, n_kv_tiles, sl2)
+#define MQA_PREFILL_LAUNCH(C, F)                                                                              \
+    hipLaunchKernelGGL((prefill_bf16_kernel<DK, DV, NR, NW, KT, C, F>), grid, dim3(NW * 64), 0, a.stream,    \
+                       (const bf16*)a.q, (const bf16*)kvt, a.out, a.lse, a.Hq, a.Hkv, a.Tq, a.Tkv, q_off, a.G, \
+                       tok, n_tok_blocks, n_kv_tiles, sl2)
     if (a.causal) {
         if (a.out_f32) MQA_PREFILL_LAUNCH(true, true); else MQA_PREFILL_LAUNCH(true, false);
     } else {
@@ -557,46 +591,61 @@ static hipError_t launch_bf16(const PrefillArgs& a) {
     return hipGetLastError();
 }
 
-template <int D>
+template <int DK, int DV>
 static hipError_t launch_f32(const PrefillArgs& a) {
-    const int n_blocks = (a.T + 15) / 16;
+    const int n_blocks = (a.Tq + 15) / 16;
     const dim3 grid(n_blocks, a.Hq, a.B);
     const float sl2 = a.scale * kLog2e;
+    const int q_off = a.Tkv - a.Tq;
     if (a.causal)
-        hipLaunchKernelGGL((prefill_f32_kernel<D, true>), grid, dim3(256), 0, a.stream, (const float*)a.q,
-                           (const float*)a.k, (const float*)a.v, (float*)a.out, a.lse, a.Hq, a.Hkv, a.T, a.G, sl2);
+        hipLaunchKernelGGL((prefill_f32_kernel<DK, DV, true>), grid, dim3(256), 0, a.stream, (const float*)a.q,
+                           (const float*)a.k, (const float*)a.v, (float*)a.out, a.lse, a.Hq, a.Hkv, a.Tq, a.Tkv,
+                           q_off, a.G, sl2);
     else
-        hipLaunchKernelGGL((prefill_f32_kernel<D, false>), grid, dim3(256), 0, a.stream, (const float*)a.q,
-                           (const float*)a.k, (const float*)a.v, (float*)a.out, a.lse, a.Hq, a.Hkv, a.T, a.G, sl2);
+        hipLaunchKernelGGL((prefill_f32_kernel<DK, DV, false>), grid, dim3(256), 0, a.stream, (const float*)a.q,
+                           (const float*)a.k, (const float*)a.v, (float*)a.out, a.lse, a.Hq, a.Hkv, a.Tq, a.Tkv,
+                           q_off, a.G, sl2);
     return hipGetLastError();
 }
 
-PrefillPlan prefill_plan(int head_dim, int in_bf16) {
+PrefillPlan prefill_plan(int d_qk, int d_v, int in_bf16) {
     PrefillPlan p{};
-    if (!in_bf16) { p.rows_per_wg = 1 << 30; p.kt = 0; return p; }
-    if (head_dim == 512) { p.rows_per_wg = 4 * 32 * 1; p.kt = 32; }
-    else if (head_dim == 128) { p.rows_per_wg = 8 * 32 * 1; p.kt = 32; }
+    if (!in_bf16) {
+        // fp32: equal widths (multiples of 64 up to 512) or the 192 / 128 pair
+        const bool ok = d_qk % 64 == 0 && d_v % 64 == 0 && d_qk <= 512 && d_v <= 512 &&
+                        (d_qk == d_v || (d_qk == 192 && d_v == 128));
+        p.rows_per_wg = ok ? (1 << 30) : 0;
+        p.kt = 0;
+        return p;
+    }
+    if (d_qk == 512 && d_v == 512) { p.rows_per_wg = 4 * 32 * 1; p.kt = 32; }
+    else if (d_qk == 128 && d_v == 128) { p.rows_per_wg = 8 * 32 * 1; p.kt = 32; }
+    else if (d_qk == 192 && d_v == 128) { p.rows_per_wg = 8 * 32 * 1; p.kt = 32; }
     return p;
 }
 
 hipError_t prefill_launch(const PrefillArgs& a) {
     if (!a.in_bf16) {
-        switch (a.D) {
-            case 64: return launch_f32<64>(a);
-            case 128: return launch_f32<128>(a);
-            case 192: return launch_f32<192>(a);
-            case 256: return launch_f32<256>(a);
-            case 320: return launch_f32<320>(a);
-            case 384: return launch_f32<384>(a);
-            case 448: return launch_f32<448>(a);
-            case 512: return launch_f32<512>(a);
+        if (a.DK == 192 && a.DV == 128) return launch_f32<192, 128>(a);
+        if (a.DK != a.DV) return hipErrorInvalidValue;
+        switch (a.DK) {
+            case 64: return launch_f32<64, 64>(a);
+            case 128: return launch_f32<128, 128>(a);
+            case 192: return launch_f32<192, 192>(a);
+            case 256: return launch_f32<256, 256>(a);
+            case 320: return launch_f32<320, 320>(a);
+            case 384: return launch_f32<384, 384>(a);
+            case 448: return launch_f32<448, 448>(a);
+            case 512: return launch_f32<512, 512>(a);
             default: return hipErrorInvalidValue;
         }
     }
-    if (a.D == 512) return launch_bf16<512, 1, 4, 32>(a);
-    // d = 128: eight waves of one 32-row tile each (192 registers, two
-    // waves per SIMD, so one wave's softmax overlaps the other's MFMAs)
-    if (a.D == 128) return launch_bf16<128, 1, 8, 32>(a);
+    if (a.DK == 512 && a.DV == 512) return launch_bf16<512, 512, 1, 4, 32>(a);
+    // 128 and 192 / 128: eight waves of one 32-row tile each (at most 256
+    // registers, two waves per SIMD, so one wave's softmax overlaps the
+    // other's MFMAs)
+    if (a.DK == 128 && a.DV == 128) return launch_bf16<128, 128, 1, 8, 32>(a);
+    if (a.DK == 192 && a.DV == 128) return launch_bf16<192, 128, 1, 8, 32>(a);
     return hipErrorInvalidValue;
 }
 

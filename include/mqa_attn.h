@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define MQA_ATTN_ABI_VERSION 1
+#define MQA_ATTN_ABI_VERSION 2
 
 typedef enum {
     MQA_DTYPE_F32 = 0,
@@ -100,6 +100,43 @@ int mqa_prefill(const void* q, const void* k, const void* v, void* out, float* l
                 int B, int Hq, int Hkv, int T, int head_dim, float scale, int causal,
                 int in_dtype, int out_dtype,
                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------ general prefill
+ * The same attention with separate query / key lengths and separate
+ * query-key / value widths:
+ *   q [B, Hq, T_q, d_qk]   k [B, Hkv, T_kv, d_qk]   v [B, Hkv, T_kv, d_v]
+ *   out [B, Hq, T_q, d_v]  lse [B, Hq, T_q] fp32 or NULL
+ *   causal != 0: the T_q queries are the LAST T_q tokens of the T_kv-token
+ *   sequence (bottom-right alignment): query i sits at position
+ *   T_kv - T_q + i and sees key j iff j <= T_kv - T_q + i.  T_q == T_kv is
+ *   the square mask of mqa_prefill; T_q < T_kv is a block of new tokens
+ *   after T_kv - T_q earlier ones whose keys and values are in k / v
+ *   (chunked prefill, several decode tokens at once).  The pages show only
+ *   the square case ("GQA和MLA详解" (lzwjava.github.io) §1); this alignment
+ *   is the reading that keeps a chunk's rows equal to the matching rows of
+ *   the whole sequence's prefill.  causal with T_q > T_kv is rejected
+ *   (MQA_ERR_INVALID_ARG: a query would see no key).
+ *   d_qk != d_v is the expanded (MHA-mode) MLA prefill: per-head keys
+ *   [c_kv W_UK[h] | k_pe] of 128 + 64 = 192 values, per-head values
+ *   c_kv W_UV[h] of 128, Hq = Hkv = 128, scale 1/sqrt(192)
+ *   ("带你了解Attention,从MHA到DeepSeek" (api.makesence.top) §4.4, prefill
+ *   expanded and decode absorbed; dimensions as in walkerchi.com "Full 路线"
+ *   §四 4.2).
+ * Supported: everything mqa_prefill supports (d_qk == d_v, as listed there),
+ *   plus (d_qk, d_v) = (192, 128) with any G <= 256 (bf16) or any G (fp32).
+ *   T_q == 0 or B == 0 is an empty call; T_kv == 0 with T_q > 0 is rejected.
+ * Workspace (bf16): `mqa_prefill_ex_workspace_size()` bytes =
+ *   B * Hkv * ceil(T_kv/32) * 32 * (d_qk + d_v) * 2; F32 needs none.
+ * mqa_prefill(..., T, head_dim, ...) is exactly
+ * mqa_prefill_ex(..., T, T, head_dim, head_dim, ...).
+ */
+size_t mqa_prefill_ex_workspace_size(int B, int Hq, int Hkv, int T_q, int T_kv,
+                                     int d_qk, int d_v, int in_dtype);
+
+int mqa_prefill_ex(const void* q, const void* k, const void* v, void* out, float* lse,
+                   int B, int Hq, int Hkv, int T_q, int T_kv, int d_qk, int d_v,
+                   float scale, int causal, int in_dtype, int out_dtype,
+                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* ----------------------------------------------------------------- decode
  * One new query token per sequence against a KV cache (split-KV: the valid

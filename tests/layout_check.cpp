@@ -101,7 +101,7 @@ int main() {
         }
         return true;
     };
-    for (int rc : {4, 8, 16, 64}) {
+    for (int rc : {4, 8, 16, 24, 64}) {
         for (int blk = 0; blk < 16; ++blk)
             for (int ks = 0; ks < rc / 2; ++ks) {
                 auto addr = [&](int l) {
@@ -115,6 +115,10 @@ int main() {
             std::set<int> s;
             for (int c = 0; c < rc; ++c) s.insert(c ^ swz32(r, rc));
             if ((int)s.size() != rc || *s.rbegin() != rc - 1) return fail("swz32 bijection", rc, r);
+            // each chunk stays inside its aligned swizzle group
+            const int gs = swz32_group(rc);
+            for (int c = 0; c < rc; ++c)
+                if ((c ^ swz32(r, rc)) / gs != c / gs) return fail("swz32 group", rc, r);
         }
     }
     // 7. Padded 1 KB rows: lane l reads row position l % 32 (key

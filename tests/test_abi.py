@@ -28,14 +28,14 @@ def _declared_functions():
 
 def test_header_functions_are_exported():
     names = _declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 11, names
     assert sorted(names) == sorted(mqa.EXPORTED_SYMBOLS)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings():
-    assert lib.mqa_attn_abi_version() == 1
+    assert lib.mqa_attn_abi_version() == 2
     for s in (OK, INVALID, UNSUPPORTED, WORKSPACE, -4, 7):
         assert lib.mqa_status_string(s)
     assert lib.mqa_last_hip_error_name() == b"hipSuccess"
@@ -79,6 +79,48 @@ def test_prefill_workspace_size():
     assert lib.mqa_prefill_workspace_size(2, 16, 1, 4096, 512, BF16) == 2 * 2 * 1 * 4096 * 512 * 2
     assert lib.mqa_prefill_workspace_size(1, 8, 2, 33, 128, BF16) == 2 * 1 * 2 * 64 * 128 * 2
     assert lib.mqa_prefill_workspace_size(1, 16, 1, 128, 512, F32) == 0
+
+
+def _prefill_ex(q=P, k=P, v=P, out=P, lse=None, B=1, Hq=128, Hkv=128, Tq=64, Tkv=256, DK=192, DV=128,
+                scale=0.072, causal=1, din=BF16, dout=BF16, ws=P, wsb=1 << 40):
+    return lib.mqa_prefill_ex(q, k, v, out, lse, B, Hq, Hkv, Tq, Tkv, DK, DV, scale, causal, din, dout, ws, wsb,
+                              None)
+
+
+def test_prefill_ex_rejections():
+    assert _prefill_ex(Tq=300, Tkv=256) == INVALID         # causal: a query would see no key
+    assert _prefill_ex(Tq=64, Tkv=0) == INVALID            # causal and non-causal: no keys
+    assert _prefill_ex(Tq=64, Tkv=0, causal=0) == INVALID
+    assert _prefill_ex(Tq=-1) == INVALID
+    assert _prefill_ex(DV=0) == INVALID
+    assert _prefill_ex(Hkv=3) == INVALID
+    assert _prefill_ex(scale=0.0) == INVALID
+    assert _prefill_ex(DK=192, DV=192) == UNSUPPORTED       # bf16 width pairs: 128/128, 512/512, 192/128
+    assert _prefill_ex(DK=128, DV=192) == UNSUPPORTED
+    assert _prefill_ex(DK=512, DV=128) == UNSUPPORTED
+    assert _prefill_ex(din=F32, dout=F32, DK=256, DV=128) == UNSUPPORTED
+    assert _prefill_ex(Hq=512, Hkv=1) == UNSUPPORTED        # group larger than a workgroup's rows
+    assert _prefill_ex(ws=None, wsb=0) == WORKSPACE
+    need = lib.mqa_prefill_ex_workspace_size(1, 128, 128, 64, 256, 192, 128, BF16)
+    assert _prefill_ex(wsb=need - 1) == WORKSPACE
+
+
+def test_prefill_ex_empty_and_noncausal_shapes():
+    assert _prefill_ex(Tq=0, q=None, k=None, v=None, out=None) == OK
+    assert _prefill_ex(B=0, q=None, k=None, v=None, out=None) == OK
+    assert _prefill_ex(Tq=0, Tkv=0, q=None, k=None, v=None, out=None) == OK
+
+
+def test_prefill_ex_workspace_size():
+    # K tile (d_qk) and transposed V tile (d_v) per 32 keys of T_kv
+    assert lib.mqa_prefill_ex_workspace_size(1, 128, 128, 100, 8192, 192, 128, BF16) == 128 * 8192 * (192 + 128) * 2
+    assert lib.mqa_prefill_ex_workspace_size(2, 16, 1, 7, 33, 512, 512, BF16) == 2 * 1 * 64 * 1024 * 2
+    assert lib.mqa_prefill_ex_workspace_size(1, 128, 128, 100, 8192, 192, 128, F32) == 0
+    # the square entry point is the general one with T_q = T_kv, d_v = d_qk
+    for args in ((2, 16, 1, 4096, 512), (1, 8, 2, 33, 128)):
+        B, Hq, Hkv, T, D = args
+        assert lib.mqa_prefill_workspace_size(B, Hq, Hkv, T, D, BF16) == \
+            lib.mqa_prefill_ex_workspace_size(B, Hq, Hkv, T, T, D, D, BF16)
 
 
 def _decode(q=P, k=P, v=P, sl=P, out=P, lse=None, B=64, Hq=16, Hkv=1, L=8192, D=512, scale=0.05,

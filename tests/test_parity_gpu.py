@@ -143,6 +143,92 @@ def test_prefill_bf16_full_size_sampled(torch, mqa, B, Hq, Hkv, T, D):
 
 
 # ---------------------------------------------------------------------------
+# general prefill: T_q != T_kv (bottom-right causal) and d_v != d_qk
+# ---------------------------------------------------------------------------
+
+PREFILL_EX_SMALL = [
+    # B, Hq, Hkv, T_q, T_kv, d_qk, d_v, causal, out dtype
+    (1, 4, 4, 300, 300, 192, 128, True, "bf16"),      # expanded MLA prefill, 2 token blocks, ragged tail
+    (2, 3, 3, 77, 77, 192, 128, True, "f32"),
+    (1, 8, 8, 130, 530, 192, 128, True, "bf16"),      # a chunk of 130 new tokens after 400
+    (1, 2, 2, 100, 100, 192, 128, False, "bf16"),
+    (2, 16, 1, 100, 777, 512, 512, True, "bf16"),     # MQA chunked prefill
+    (1, 16, 1, 1, 300, 512, 512, True, "f32"),        # one new token
+    (1, 64, 8, 200, 1000, 128, 128, True, "bf16"),    # GQA chunk
+    (1, 16, 2, 33, 500, 128, 128, False, "bf16"),     # no mask, T_q < T_kv
+    (1, 16, 1, 64, 40, 512, 512, False, "bf16"),      # no mask, T_q > T_kv
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Tq,Tkv,DK,DV,causal,odt", PREFILL_EX_SMALL)
+def test_prefill_ex_bf16_small(torch, mqa, B, Hq, Hkv, Tq, Tkv, DK, DV, causal, odt):
+    _say(f"prefill_ex bf16 B{B} Hq{Hq} Hkv{Hkv} Tq{Tq} Tkv{Tkv} DK{DK} DV{DV} causal={causal} out={odt}")
+    q, k, v = prefill_inputs(B, Hq, Hkv, Tq, DK, "bf16", seed=3, d_v=DV, T_kv=Tkv)
+    lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device="cuda")
+    out_dtype = torch.float32 if odt == "f32" else torch.bfloat16
+    out = mqa.mqa_prefill_ex(dev(torch, q), dev(torch, k), dev(torch, v), causal=causal, lse=lse,
+                             out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    assert out.shape == (B, Hq, Tq, DV)
+    ref, ref_lse = oracle.prefill_ref(q.f32(), k.f32(), v.f32(), 1 / math.sqrt(DK), causal)
+    assert np.all(np.isfinite(host(out)))
+    assert _maxerr(host(out), ref) <= BF16_TOL
+    assert _maxerr(host(lse), ref_lse) <= BF16_TOL
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_ex_f32(torch, mqa, causal):
+    """fp32 end to end: expanded-MLA widths and a chunk (T_q < T_kv)."""
+    for B, Hq, Hkv, Tq, Tkv, DK, DV in ((2, 4, 2, 37, 90, 192, 128), (1, 6, 3, 20, 61, 128, 128),
+                                        (1, 16, 1, 5, 5, 192, 128)):
+        _say(f"prefill_ex f32 B{B} Hq{Hq} Hkv{Hkv} Tq{Tq} Tkv{Tkv} DK{DK} DV{DV} causal={causal}")
+        q, k, v = prefill_inputs(B, Hq, Hkv, Tq, DK, "f32", seed=4, d_v=DV, T_kv=Tkv)
+        lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device="cuda")
+        out = mqa.mqa_prefill_ex(dev(torch, q), dev(torch, k), dev(torch, v), causal=causal, scale=0.11,
+                                 lse=lse)
+        torch.cuda.synchronize()
+        ref, ref_lse = oracle.prefill_ref(q.f32(), k.f32(), v.f32(), 0.11, causal)
+        assert _maxerr(host(out), ref) <= F32_TOL
+        assert _maxerr(host(lse), ref_lse) <= F32_TOL
+
+
+def test_prefill_ex_square_matches_prefill(torch, mqa):
+    """mqa_prefill_ex with T_q = T_kv and d_v = d_qk is the square entry point,
+    bit for bit."""
+    _say("prefill_ex square vs prefill B1 Hq16 Hkv1 T150 D512")
+    q, k, v = prefill_inputs(1, 16, 1, 150, 512, "bf16", seed=5)
+    dq, dk, dv = dev(torch, q), dev(torch, k), dev(torch, v)
+    a = mqa.mqa_prefill(dq, dk, dv, causal=True)
+    b = mqa.mqa_prefill_ex(dq, dk, dv, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Tq,Tkv,DK,DV", [(1, 128, 128, 8192, 8192, 192, 128),
+                                                  (2, 16, 1, 1024, 8192, 512, 512)])
+def test_prefill_ex_full_size_sampled(torch, mqa, B, Hq, Hkv, Tq, Tkv, DK, DV):
+    """Full-size expanded MLA prefill (H=128, d 192/128, T=8192) and MQA
+    chunked prefill (1024 new tokens after 7168, d=512), causal, in the
+    bench's launch configuration: sampled rows vs the oracle and bitwise
+    run-to-run repeatability."""
+    _say(f"prefill_ex bf16 full B{B} Hq{Hq} Hkv{Hkv} Tq{Tq} Tkv{Tkv} DK{DK} DV{DV}")
+    q, k, v = prefill_inputs(B, Hq, Hkv, Tq, DK, "bf16", seed=0, d_v=DV, T_kv=Tkv)
+    dq, dk, dv = dev(torch, q), dev(torch, k), dev(torch, v)
+    lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device="cuda")
+    out = mqa.mqa_prefill_ex(dq, dk, dv, causal=True, lse=lse)
+    out2 = mqa.mqa_prefill_ex(dq, dk, dv, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    rows = _sample_rows(B, Hq, Tq, 40, seed=6)
+    ref, ref_lse = oracle.prefill_rows_ref(q.f32(), k.f32(), v.f32(), rows, 1 / math.sqrt(DK), True)
+    got = np.stack([host(out[b, h, i]) for b, h, i in rows])
+    got_lse = np.array([float(lse[b, h, i]) for b, h, i in rows])
+    assert _maxerr(got, ref) <= BF16_TOL
+    assert _maxerr(got_lse, ref_lse) <= BF16_TOL
+    assert bool(torch.isfinite(out.float()).all())
+
+
+# ---------------------------------------------------------------------------
 # decode
 # ---------------------------------------------------------------------------
 
