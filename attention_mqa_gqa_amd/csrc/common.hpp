@@ -33,6 +33,10 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// MI355X (gfx950) has 8 XCDs of 32 compute units, each XCD with its own L2;
+// the dispatcher deals workgroups to the XCDs round-robin by flat index.
+// Only locality depends on this value, never correctness.
+constexpr int kNumXcd = 8;
 // Lazy rescaling: the running row maximum used for exponentiation is only
 // raised when a new score exceeds it by more than this many log2 units, so
 // probabilities stay below 2^kRescaleSlack and the accumulator rescale is

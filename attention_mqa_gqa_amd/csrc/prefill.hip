@@ -108,7 +108,7 @@ template <int DK, int DV, int NR, int NW, int KT, bool CAUSAL, bool OUT_F32>
 __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ KVt,
     void* __restrict__ Out, float* __restrict__ Lse, int Hq, int Hkv, int Tq, int Tkv, int q_off,
-    int G, int tok_per_wg, int n_tok_blocks, int n_kv_tiles, float scale_log2) {
+    int G, int tok_per_wg, int n_tok_blocks, int n_kv_tiles, int xcd_map, float scale_log2) {
     constexpr int RW = 32 * NR;           // rows per wave
     constexpr int KS = DK / 16;           // QK^T contraction steps
     constexpr int MT_O = DV / 32;         // O^T M-tiles (value dims)
@@ -146,12 +146,37 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     const int w = wave_id();
     const int h2 = lane >> 5;             // lane half
     const int n = lane & 31;              // row (column of the 32x32 tile)
-    const int tb = CAUSAL ? (n_tok_blocks - 1 - (int)blockIdx.x) : (int)blockIdx.x;
-    const int hk = blockIdx.y;
-    const int b = blockIdx.z;
+    // Workgroup -> (batch, KV head, token block).  Workgroups are dealt to
+    // the XCDs round-robin by flat index f (XCD f % 8, its slot-th one).  The
+    // maps keep the K/V tiles an XCD re-reads in its own L2:
+    //   xcd_map 1 (pairs P = B*Hkv a multiple of 8): every XCD takes whole
+    //     (batch, KV head) pairs, blocks of a pair heaviest first;
+    //   xcd_map 2 (8 a multiple of P, blocks a multiple of 8/P): each pair
+    //     gets 8/P XCDs and their slots deal its blocks heaviest first;
+    //   otherwise the launch grid's own order.
+    int blk, hk, b;
+    if (xcd_map != 0) {
+        const int f = (int)(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
+        const int x = f % kNumXcd, slot = f / kNumXcd;
+        int pair;
+        if (xcd_map == 1) {
+            pair = (slot / n_tok_blocks) * kNumXcd + x;
+            blk = slot % n_tok_blocks;
+        } else {
+            const int P = (int)(gridDim.y * gridDim.z);
+            pair = x % P;
+            blk = slot * (kNumXcd / P) + x / P;
+        }
+        hk = pair % Hkv;
+        b = pair / Hkv;
+    } else {
+        blk = blockIdx.x;
+        hk = blockIdx.y;
+        b = blockIdx.z;
+    }
+    const int tb = CAUSAL ? (n_tok_blocks - 1 - blk) : blk;     // heaviest blocks first
     const int t0 = tb * tok_per_wg;
     const int rows_used = tok_per_wg * G;
-    (void)n_tok_blocks;
 
     int row_tok[NR];
     int row_head[NR];
@@ -578,10 +603,12 @@ static hipError_t launch_bf16(const PrefillArgs& a) {
                        (const bf16*)a.k, (const bf16*)a.v, kvt, a.Tkv, n_kv_tiles);
     const dim3 grid(n_tok_blocks, a.Hkv, a.B);
     const float sl2 = a.scale * kLog2e;
+    const int P = a.B * a.Hkv;
+    const int xcd_map = P % kNumXcd == 0 ? 1 : (kNumXcd % P == 0 && n_tok_blocks % (kNumXcd / P) == 0 ? 2 : 0);
 #define MQA_PREFILL_LAUNCH(C, F)                                                                              \
     hipLaunchKernelGGL((prefill_bf16_kernel<DK, DV, NR, NW, KT, C, F>), grid, dim3(NW * 64), 0, a.stream,    \
                        (const bf16*)a.q, (const bf16*)kvt, a.out, a.lse, a.Hq, a.Hkv, a.Tq, a.Tkv, q_off, a.G, \
-                       tok, n_tok_blocks, n_kv_tiles, sl2)
+                       tok, n_tok_blocks, n_kv_tiles, xcd_map, sl2)
     if (a.causal) {
         if (a.out_f32) MQA_PREFILL_LAUNCH(true, true); else MQA_PREFILL_LAUNCH(true, false);
     } else {

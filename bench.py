@@ -8,11 +8,15 @@ workload, inputs already resident in HBM:
   * mqa_decode           GQA, batch 128, Hq=64, Hkv=8, d=128, cache
                          lengths uniform in [1024, 16384]
   * mla_decode_absorbed  batch 32, H=128, latent 576 (V = first 512), ctx 32768
+  * mqa_prefill_ex       expanded MLA prefill, causal, B=1, H=128 (MHA),
+                         T=8192, q/k 192 wide, v 128 wide
+  * mqa_prefill_ex       chunked causal MQA prefill, B=2, Hq=16, Hkv=1,
+                         d=512, 1024 new tokens after 7168 (bottom-right)
 all bf16 in, fp32 accumulation, bf16 out.
 
 Every call is bracketed with HIP events on the stream it is launched on.
 The headline `value` is the causal MQA prefill TFLOP/s (visible query/key
-pairs only, 4 d flops per pair); the other workloads sit beside it, each
+pairs only, 2 (d_qk + d_v) flops per pair); the other workloads sit beside it, each
 with its roofline.  `roofline.traffic` is the HBM traffic per call measured
 with rocprofv3 counters (profiles/traffic.json), reported only while the
 kernel sources still hash to the value recorded with the counters.
@@ -50,16 +54,24 @@ ORDER = (
     ("gqa_prefill_bf16_b1_t8192", "gqa_prefill"),
     ("gqa_decode_bf16_b128_l1024to16384", "gqa_decode"),
     ("mla_decode_bf16_b32_l32768", "mla_decode"),
+    ("mla_prefill_bf16_b1_h128_t8192", "mla_prefill"),
+    ("mqa_chunk_prefill_bf16_b2_q1024_kv8192", "chunk_prefill"),
 )
 
 
-def prefill_flops(B, Hq, T, D, causal=True, **_):
-    pairs = T * (T + 1) // 2 if causal else T * T
-    return B * Hq * pairs * 2 * (D + D)
+def prefill_flops(B, Hq, T, D, causal=True, T_kv=None, DV=None, **_):
+    """Visible (query, key) pairs x 2 (d_qk + d_v).  Causal with T queries
+    after T_kv - T earlier tokens: query i sees T_kv - T + i + 1 keys."""
+    T_kv = T if T_kv is None else T_kv
+    DV = D if DV is None else DV
+    pairs = T * (T_kv - T) + T * (T + 1) // 2 if causal else T * T_kv
+    return B * Hq * pairs * 2 * (D + DV)
 
 
-def prefill_bytes(B, Hq, Hkv, T, D, **_):
-    return (2 * B * Hq * T * D + 2 * B * Hkv * T * D) * 2      # q, out, k, v (bf16)
+def prefill_bytes(B, Hq, Hkv, T, D, T_kv=None, DV=None, **_):
+    T_kv = T if T_kv is None else T_kv
+    DV = D if DV is None else DV
+    return (B * Hq * T * (D + DV) + B * Hkv * T_kv * (D + DV)) * 2      # q, out, k, v (bf16)
 
 
 def decode_bytes(B, Hq, Hkv, D, seq_lens, **_):
@@ -190,14 +202,20 @@ def main():
         wl = WORKLOADS[name]
         s = dict(wl.shape)
         if wl.kind == "prefill":
-            q, k, v = prefill_inputs(s["B"], s["Hq"], s["Hkv"], s["T"], s["D"], "bf16", seed=0)
+            T_kv, DV = s.get("T_kv", s["T"]), s.get("DV", s["D"])
+            q, k, v = prefill_inputs(s["B"], s["Hq"], s["Hkv"], s["T"], s["D"], "bf16", seed=0, d_v=DV, T_kv=T_kv)
             dq, dk, dv = to_dev(q), to_dev(k), to_dev(v)
-            out = torch.empty((s["B"], s["Hq"], s["T"], s["D"]), dtype=torch.bfloat16, device=dev)
-            ws = torch.empty(max(1, mqa.mqa_prefill_workspace_size(s["B"], s["Hq"], s["Hkv"], s["T"], s["D"],
-                                                                   mqa.DTYPE_BF16)), dtype=torch.uint8, device=dev)
+            out = torch.empty((s["B"], s["Hq"], s["T"], DV), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(max(1, mqa.mqa_prefill_ex_workspace_size(s["B"], s["Hq"], s["Hkv"], s["T"], T_kv, s["D"],
+                                                                      DV, mqa.DTYPE_BF16)),
+                             dtype=torch.uint8, device=dev)
             sc = s["D"] ** -0.5
-            calls[name] = (lambda dq=dq, dk=dk, dv=dv, out=out, ws=ws, sc=sc:
-                           mqa.mqa_prefill(dq, dk, dv, causal=True, scale=sc, out=out, workspace=ws))
+            if T_kv == s["T"] and DV == s["D"]:
+                calls[name] = (lambda dq=dq, dk=dk, dv=dv, out=out, ws=ws, sc=sc:
+                               mqa.mqa_prefill(dq, dk, dv, causal=True, scale=sc, out=out, workspace=ws))
+            else:
+                calls[name] = (lambda dq=dq, dk=dk, dv=dv, out=out, ws=ws, sc=sc:
+                               mqa.mqa_prefill_ex(dq, dk, dv, causal=True, scale=sc, out=out, workspace=ws))
             work[name] = dict(flops=prefill_flops(**s), bytes=prefill_bytes(**s), bound="mfma", shape=s)
             if name == ORDER[0][0]:
                 host[name] = (q, k, v, sc, s)

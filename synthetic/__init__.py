@@ -222,5 +222,11 @@ WORKLOADS = {
                  dict(B=128, Hq=64, Hkv=8, L=16384, D=128, lengths=(1024, 16384))),
         Workload("mla_decode_bf16_b32_l32768", "mla", "bf16",
                  dict(B=32, H=128, L=32768, D=576)),
+        # expanded (MHA-mode) MLA prefill: 128 heads, q/k 128 + 64 wide, v 128
+        Workload("mla_prefill_bf16_b1_h128_t8192", "prefill", "bf16",
+                 dict(B=1, Hq=128, Hkv=128, T=8192, D=192, DV=128)),
+        # chunked MQA prefill: 1024 new tokens after 7168 cached ones
+        Workload("mqa_chunk_prefill_bf16_b2_q1024_kv8192", "prefill", "bf16",
+                 dict(B=2, Hq=16, Hkv=1, T=1024, T_kv=8192, D=512)),
     )
 }
