@@ -18,6 +18,10 @@ be checked against the pages by eye.  Sources (page title, section):
   MQA operator, section "head_dim = 512 为什么值得注意"; makesence §3.1.
 * MLA latent cache, matrix absorption and decoupled RoPE key: lzwjava §3,
   makesence §4.3 and §4.5, walkerchi §四 4.2-4.3.
+* MLA prefill in the expanded (MHA) form and decode in the absorbed form:
+  makesence §4.4; sparse (top-k) attention over the MLA cache: makesence §5.1.
+* chunked prefill (queries = the last T of S tokens, bottom-right causal
+  mask): a reading; the pages show only the square mask (lzwjava §1).
 
 Parity status: every function is pinned by ``tests/test_oracle.py``
 (brute force, closed forms, invariants, page values); none is unpinned.
@@ -30,6 +34,7 @@ from .attention_ref import (  # noqa: F401
     lse_merge,
     mla_absorbed_ref,
     mla_explicit_ref,
+    mla_sparse_ref,
     partial_ref,
     prefill_ref,
     prefill_rows_ref,

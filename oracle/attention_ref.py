@@ -34,6 +34,7 @@ __all__ = [
     "partial_ref",
     "lse_merge",
     "mla_absorbed_ref",
+    "mla_sparse_ref",
     "absorb_query",
     "mla_explicit_ref",
     "kv_values_per_token",
@@ -228,6 +229,37 @@ def mla_absorbed_ref(q_abs, kv_cache, seq_lens, scale, d_v=512):
         rows = _f64(kv_cache[b, :L])                     # [L, 576]
         o, s = _attend(_f64(q_abs[b]), rows, rows[:, :d_v], scale,
                        np.ones((H, L), dtype=bool))
+        out[b], lse[b] = o, s
+    return out, lse
+
+
+def mla_sparse_ref(q_abs, kv_cache, indices, scale, d_v=512):
+    """Absorbed MLA decode over a selected subset of the cached rows.
+
+    DeepSeek sparse attention keeps the MLA cache and lets each query attend
+    only to k selected tokens (makesence §5.1: an indexer picks the top-k
+    positions, k = 2048 in V3.2).  Here the selection is an input: sequence b
+    attends to the rows ``kv_cache[b, indices[b, j]]``; entries outside
+    [0, L_max) (e.g. -1 padding for sequences with fewer than k tokens) are
+    skipped, and a row listed twice counts twice (the attended set is the
+    list as given).  Each attended row is used as in :func:`mla_absorbed_ref`
+    (whole row = key, first ``d_v`` values = value).  A sequence with no
+    valid entry gets out = 0 and lse = -inf.
+
+    q_abs [B, H, d_c + d_R]; kv_cache [B, L_max, d_c + d_R]; indices int [B, k].
+    Returns (o_latent [B, H, d_v], lse [B, H]).
+    """
+    B, H, _ = q_abs.shape
+    L_max = kv_cache.shape[1]
+    out = np.zeros((B, H, d_v))
+    lse = np.full((B, H), -np.inf)
+    for b in range(B):
+        sel = [int(i) for i in indices[b] if 0 <= int(i) < L_max]
+        if not sel:
+            continue
+        rows = _f64(kv_cache[b, sel])                    # [n, 576], gathered in list order
+        o, s = _attend(_f64(q_abs[b]), rows, rows[:, :d_v], scale,
+                       np.ones((H, len(sel)), dtype=bool))
         out[b], lse[b] = o, s
     return out, lse
 

@@ -48,6 +48,7 @@ __all__ = [
     "prefill_inputs",
     "decode_inputs",
     "mla_inputs",
+    "draw_topk",
     "draw_lengths",
     "Workload",
     "WORKLOADS",
@@ -194,6 +195,20 @@ def mla_inputs(B, H, L_max, d_kv=576, dtype="bf16", seed=0, lengths=None,
     return Tensor(q, dtype), kv, seq_lens
 
 
+def draw_topk(B, seq_lens, topk, seed):
+    """Selected positions int32 [B, topk]: for sequence b, min(topk, L_b)
+    distinct positions drawn uniformly from [0, L_b) with
+    ``default_rng([seed, 98, b]).choice(L_b, n, replace=False)``, sorted
+    ascending, then -1 padding."""
+    idx = np.full((B, topk), -1, dtype=np.int32)
+    for b in range(B):
+        L = int(seq_lens[b])
+        n = min(topk, L)
+        sel = np.random.default_rng([seed, 98, b]).choice(L, size=n, replace=False)
+        idx[b, :n] = np.sort(sel).astype(np.int32)
+    return idx
+
+
 def mla_slice(seed, b, H, L, d_kv=576):
     """float32 draws of sequence b only: (q_abs [H,d_kv], latent [L,d_kv])."""
     return _draw(seed, 0, b, (H, d_kv)), _draw(seed, 1, b, (L, d_kv))
@@ -222,6 +237,9 @@ WORKLOADS = {
                  dict(B=128, Hq=64, Hkv=8, L=16384, D=128, lengths=(1024, 16384))),
         Workload("mla_decode_bf16_b32_l32768", "mla", "bf16",
                  dict(B=32, H=128, L=32768, D=576)),
+        # sparse (top-k) MLA decode: 2048 selected rows of a 32768-row cache
+        Workload("mla_sparse_decode_bf16_b32_l32768_k2048", "mla_sparse", "bf16",
+                 dict(B=32, H=128, L=32768, D=576, topk=2048)),
         # expanded (MHA-mode) MLA prefill: 128 heads, q/k 128 + 64 wide, v 128
         Workload("mla_prefill_bf16_b1_h128_t8192", "prefill", "bf16",
                  dict(B=1, Hq=128, Hkv=128, T=8192, D=192, DV=128)),

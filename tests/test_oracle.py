@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 import oracle
-from synthetic import prefill_inputs, decode_inputs, mla_inputs, round_bf16, bf16_bits, bf16_to_f32
+from synthetic import prefill_inputs, decode_inputs, mla_inputs, draw_topk, round_bf16, bf16_bits, bf16_to_f32
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -477,6 +477,67 @@ def test_mla_ignores_padding_and_uses_leading_latent_as_value():
     a, _ = oracle.mla_absorbed_ref(qz, kv.f32(), lens, 0.5, d_v=8)
     b, _ = oracle.mla_absorbed_ref(qz, kv2, lens, 0.5, d_v=8)
     assert np.max(np.abs(a - b)) <= 1e-14
+
+
+# ---------------------------------------------------------------------------
+# Sparse (top-k) MLA decode: attention over the listed cache rows only
+# (makesence §5.1).
+# ---------------------------------------------------------------------------
+
+def test_sparse_mla_brute_force_duplicates_and_skips():
+    """Pure-Python loop over the listed rows: -1 and out-of-range entries are
+    skipped, a row listed twice enters the softmax twice."""
+    rng = np.random.default_rng(36)
+    B, H, L, DK, DV = 2, 3, 9, 6, 4
+    q = rng.standard_normal((B, H, DK))
+    kv = rng.standard_normal((B, L, DK))
+    idx = np.array([[4, 0, 4, 8, -1, 11], [2, -1, -1, 7, 3, 30]])
+    out, lse = oracle.mla_sparse_ref(q, kv, idx, 0.4, d_v=DV)
+    listed = [[4, 0, 4, 8], [2, 7, 3]]
+    for b in range(B):
+        for h in range(H):
+            keys = [list(kv[b, j]) for j in listed[b]]
+            vals = [list(kv[b, j, :DV]) for j in listed[b]]
+            o, s_ = _brute_row(list(q[b, h]), keys, vals, 0.4)
+            assert np.max(np.abs(out[b, h] - np.array(o))) <= 1e-12
+            assert abs(lse[b, h] - s_) <= 1e-12
+
+
+def test_sparse_mla_all_rows_equals_dense():
+    """Listing every valid row (then -1 padding) is the dense absorbed decode."""
+    q, kv, lens = mla_inputs(2, 4, 10, d_kv=12, dtype="f32", seed=37, lengths=(3, 9))
+    idx = np.full((2, 10), -1)
+    for b in range(2):
+        idx[b, :lens[b]] = np.arange(lens[b])
+    sp, lsp = oracle.mla_sparse_ref(q.f32(), kv.f32(), idx, 0.5, d_v=8)
+    de, lde = oracle.mla_absorbed_ref(q.f32(), kv.f32(), lens, 0.5, d_v=8)
+    assert np.max(np.abs(sp - de)) <= 1e-13
+    assert np.max(np.abs(lsp - lde)) <= 1e-13
+
+
+def test_sparse_mla_order_invariant_and_empty():
+    q, kv, lens = mla_inputs(3, 4, 20, d_kv=12, dtype="f32", seed=38)
+    idx = draw_topk(3, lens, 7, seed=38)
+    base, lb = oracle.mla_sparse_ref(q.f32(), kv.f32(), idx, 0.5, d_v=8)
+    perm = idx[:, ::-1].copy()
+    p_, lp = oracle.mla_sparse_ref(q.f32(), kv.f32(), perm, 0.5, d_v=8)
+    assert np.max(np.abs(p_ - base)) <= 1e-13 and np.max(np.abs(lp - lb)) <= 1e-13
+    idx2 = idx.copy()
+    idx2[1] = -1                                  # sequence 1 selects nothing
+    e, le = oracle.mla_sparse_ref(q.f32(), kv.f32(), idx2, 0.5, d_v=8)
+    assert np.all(e[1] == 0) and np.all(le[1] == -np.inf)
+    assert np.array_equal(e[[0, 2]], base[[0, 2]])
+
+
+def test_draw_topk_selects_distinct_positions():
+    lens = np.array([50, 5, 8])
+    idx = draw_topk(3, lens, 8, seed=3)
+    for b in range(3):
+        sel = idx[b][idx[b] >= 0]
+        assert len(sel) == min(8, lens[b])
+        assert len(set(sel.tolist())) == len(sel) and np.all(np.diff(sel) > 0)
+        assert sel.min() >= 0 and sel.max() < lens[b]
+        assert np.all(idx[b][len(sel):] == -1)
 
 
 # ---------------------------------------------------------------------------
