@@ -8,7 +8,8 @@ The entry points carry the C ABI's names (see ``include/mqa_attn.h``):
 * :func:`mqa_prefill_ex`       -- the same with T_q != T_kv (bottom-right
   causal) and d_v != d_qk (expanded MLA prefill);
 * :func:`mqa_decode`           -- one query token per sequence vs a KV cache;
-* :func:`mla_decode_absorbed`  -- absorbed MLA decode over a latent cache.
+* :func:`mla_decode_absorbed`  -- absorbed MLA decode over a latent cache;
+* :func:`mla_decode_sparse`    -- the same over selected (top-k) cache rows.
 
 The library must be built (``python attention_mqa_gqa_amd/build.py``); if it
 is missing or cannot be loaded, importing the bindings raises.
@@ -32,6 +33,8 @@ __all__ = [
     "mqa_decode_workspace_size",
     "mla_decode_absorbed",
     "mla_decode_workspace_size",
+    "mla_decode_sparse",
+    "mla_decode_sparse_workspace_size",
     "DTYPE_F32",
     "DTYPE_BF16",
     "EXPORTED_SYMBOLS",
@@ -55,6 +58,8 @@ EXPORTED_SYMBOLS = (
     "mqa_decode",
     "mla_decode_workspace_size",
     "mla_decode_absorbed",
+    "mla_decode_sparse_workspace_size",
+    "mla_decode_sparse",
 )
 
 
@@ -99,6 +104,10 @@ def _load():
     l.mla_decode_workspace_size.argtypes = [i, i, i]
     l.mla_decode_absorbed.restype = i
     l.mla_decode_absorbed.argtypes = [vp, vp, vp, vp, vp, i, i, i, f, i, i, vp, sz, vp]
+    l.mla_decode_sparse_workspace_size.restype = sz
+    l.mla_decode_sparse_workspace_size.argtypes = [i, i, i]
+    l.mla_decode_sparse.restype = i
+    l.mla_decode_sparse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp, sz, vp]
     return l
 
 
@@ -161,6 +170,10 @@ def mqa_decode_workspace_size(B, Hq, Hkv, max_len, head_dim):
 
 def mla_decode_workspace_size(B, H, max_len):
     return int(lib.mla_decode_workspace_size(B, H, max_len))
+
+
+def mla_decode_sparse_workspace_size(B, H, topk):
+    return int(lib.mla_decode_sparse_workspace_size(B, H, topk))
 
 
 def _workspace(nbytes, device, workspace):
@@ -285,4 +298,32 @@ def mla_decode_absorbed(q_abs, kv_cache, seq_lens, scale=None, out=None, out_dty
                                  B, H, L_max, scale, _dtype_code(q_abs.dtype), _dtype_code(out.dtype),
                                  _ptr(ws), wsb, _stream_ptr(stream, q_abs.device))
     _check(st, "mla_decode_absorbed")
+    return out
+
+
+def mla_decode_sparse(q_abs, kv_cache, indices, scale=None, out=None, out_dtype=None, lse=None,
+                      workspace=None, stream=None):
+    """q_abs [B,H,576], kv_cache [B,L_max,576], indices int32 [B,topk] (rows to
+    attend; entries outside [0, L_max) skipped) -> out [B,H,512]."""
+    torch = _torch()
+    _require(q_abs, "q_abs", 3)
+    _require(kv_cache, "kv_cache", 3)
+    _require(indices, "indices", 2)
+    if indices.dtype != torch.int32:
+        raise TypeError("indices must be int32")
+    B, H, DK = q_abs.shape
+    if DK != 576 or kv_cache.shape[0] != B or kv_cache.shape[2] != 576 or indices.shape[0] != B:
+        raise ValueError("q_abs must be [B,H,576], kv_cache [B,L_max,576] and indices [B,topk]")
+    L_max, topk = kv_cache.shape[1], indices.shape[1]
+    out_dtype = q_abs.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, H, 512), dtype=out_dtype, device=q_abs.device)
+    _require(out, "out", 3)
+    scale = 1.0 / math.sqrt(192.0) if scale is None else float(scale)
+    nbytes = mla_decode_sparse_workspace_size(B, H, topk)
+    ws, wsb = _workspace(nbytes, q_abs.device, workspace)
+    st = lib.mla_decode_sparse(_ptr(q_abs), _ptr(kv_cache), _ptr(indices), _ptr(out), _ptr(lse),
+                               B, H, L_max, topk, scale, _dtype_code(q_abs.dtype), _dtype_code(out.dtype),
+                               _ptr(ws), wsb, _stream_ptr(stream, q_abs.device))
+    _check(st, "mla_decode_sparse")
     return out

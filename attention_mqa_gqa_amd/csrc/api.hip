@@ -179,7 +179,41 @@ int mla_decode_absorbed(const void* q_abs, const void* kv_cache, const int32_t* 
     if (!workspace || workspace_bytes < need) return MQA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return MQA_ERR_INVALID_ARG;
     mqa::MlaArgs a;
-    a.q = q_abs; a.kv = kv_cache; a.seq_lens = seq_lens; a.out = out; a.lse = lse;
+    a.q = q_abs; a.kv = kv_cache; a.seq_lens = seq_lens; a.indices = nullptr; a.topk = 0; a.out = out; a.lse = lse;
+    a.B = B; a.H = H; a.max_len = max_len; a.scale = scale; a.out_f32 = out_dtype == MQA_DTYPE_F32;
+    a.part_o = (float*)workspace;
+    a.part_ml = (float*)workspace + (size_t)B * H * plan.n_split * 512;
+    a.plan = plan; a.stream = (hipStream_t)stream;
+    clear_stale_error();
+    return hip_status(mqa::mla_launch(a));
+}
+
+size_t mla_decode_sparse_workspace_size(int B, int H, int topk) {
+    if (B <= 0 || H <= 0 || topk <= 0) return 0;
+    return decode_ws_bytes(B, H, 512, mqa::mla_sparse_plan(B, topk));
+}
+
+int mla_decode_sparse(const void* q_abs, const void* kv_cache, const int32_t* indices, void* out, float* lse,
+                      int B, int H, int max_len, int topk, float scale, int dtype, int out_dtype, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    if (B < 0 || H <= 0 || max_len <= 0 || topk <= 0) return MQA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return MQA_ERR_INVALID_ARG;
+    if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return MQA_ERR_INVALID_ARG;
+    if (B == 0) return MQA_OK;
+    if (!q_abs || !kv_cache || !indices || !out) return MQA_ERR_INVALID_ARG;
+    if (!aligned16(q_abs) || !aligned16(kv_cache) || !aligned16(out) || ((uintptr_t)indices & 3u) ||
+        (lse && ((uintptr_t)lse & 3u)))
+        return MQA_ERR_INVALID_ARG;
+    if (dtype != MQA_DTYPE_BF16) return MQA_ERR_UNSUPPORTED;
+    if (H % 16 != 0 || H > 128) return MQA_ERR_UNSUPPORTED;
+    // one sequence's latent cache is addressed with 32-bit byte offsets
+    if ((size_t)max_len * 576 * 2 > 0xFFFFFFFFull) return MQA_ERR_UNSUPPORTED;
+    const DecodePlan plan = mqa::mla_sparse_plan(B, topk);
+    const size_t need = decode_ws_bytes(B, H, 512, plan);
+    if (!workspace || workspace_bytes < need) return MQA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MQA_ERR_INVALID_ARG;
+    mqa::MlaArgs a;
+    a.q = q_abs; a.kv = kv_cache; a.seq_lens = nullptr; a.indices = indices; a.topk = topk; a.out = out; a.lse = lse;
     a.B = B; a.H = H; a.max_len = max_len; a.scale = scale; a.out_f32 = out_dtype == MQA_DTYPE_F32;
     a.part_o = (float*)workspace;
     a.part_ml = (float*)workspace + (size_t)B * H * plan.n_split * 512;

@@ -219,19 +219,25 @@ __global__ __launch_bounds__(DV / 4) void lse_merge_kernel(const float* __restri
     const int h = blockIdx.x;
     const int b = blockIdx.y;
     const int d4 = threadIdx.x * 4;
-    const int L = min(max(seq_lens[b], 0), max_len);
-    const int ns = L > 0 ? (L + chunk - 1) / chunk : 0;
+    // seq_lens null: all n_split partials are present (some may be empty:
+    // m = -inf, l = 0, O = 0, which contribute nothing)
+    int ns = n_split;
+    if (seq_lens != nullptr) {
+        const int L = min(max(seq_lens[b], 0), max_len);
+        ns = L > 0 ? (L + chunk - 1) / chunk : 0;
+    }
     const size_t row = (size_t)b * H + h;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float M = -INFINITY, lsum = 0.f;
     for (int s = 0; s < ns; ++s) M = fmaxf(M, part_ml[2 * (row * n_split + s)]);
     for (int s = 0; s < ns; ++s) {
         const size_t pr = row * n_split + s;
-        const float f = fast_exp2(part_ml[2 * pr] - M);
+        const float ms = part_ml[2 * pr];
+        const float f = ms == -INFINITY ? 0.f : fast_exp2(ms - M);
         lsum += part_ml[2 * pr + 1] * f;
         acc += *(const f32x4*)(part_o + pr * DV + d4) * f;
     }
-    const float inv = ns > 0 ? 1.f / lsum : 0.f;
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     acc *= inv;
     if constexpr (OUT_F32) {
         *(f32x4*)((float*)Out + row * DV + d4) = acc;
@@ -241,7 +247,7 @@ __global__ __launch_bounds__(DV / 4) void lse_merge_kernel(const float* __restri
         pk.y = pack_bf16x2(acc.z, acc.w);
         *(u32x2*)((bf16*)Out + row * DV + d4) = pk;
     }
-    if (Lse != nullptr && threadIdx.x == 0) Lse[row] = ns > 0 ? M * kLn2 + __logf(lsum) : -INFINITY;
+    if (Lse != nullptr && threadIdx.x == 0) Lse[row] = lsum > 0.f ? M * kLn2 + __logf(lsum) : -INFINITY;
 }
 
 hipError_t merge_launch(const float* part_o, const float* part_ml, const int32_t* seq_lens, void* out, float* lse,

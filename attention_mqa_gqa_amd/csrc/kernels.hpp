@@ -42,6 +42,7 @@ struct DecodePlan {
 
 DecodePlan decode_plan(int B, int Hkv, int max_len, int head_dim);
 DecodePlan mla_plan(int B, int max_len);
+DecodePlan mla_sparse_plan(int B, int topk);
 
 struct DecodeArgs {
     const void* q;
@@ -64,7 +65,9 @@ hipError_t decode_launch(const DecodeArgs& a);
 struct MlaArgs {
     const void* q;
     const void* kv;
-    const int32_t* seq_lens;
+    const int32_t* seq_lens;   // dense: rows 0 .. seq_lens[b]-1
+    const int32_t* indices;    // sparse (non-null): rows indices[b, 0 .. topk-1]
+    int topk;
     void* out;
     float* lse;
     int B, H, max_len;

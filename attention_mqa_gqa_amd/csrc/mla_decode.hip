@@ -22,6 +22,11 @@
 //     quarter of a full-width split.  V^T operands come straight from the
 //     row-major latent tile through transposing LDS reads;
 //   * partials per (head, split) are merged by the shared log-sum-exp kernel.
+// Sparse variant (top-k attention over the same cache, makesence §5.1): the
+// rows of sequence b are kv[b, indices[b, j]] instead of kv[b, 0 .. L-1];
+// each workgroup stages its chunk of the index list in LDS, every copy
+// fetches the listed row (the direct-to-LDS copy takes any per-lane source
+// address), and list entries outside [0, max_len) are masked.
 #include "common.hpp"
 #include "layout.hpp"
 #include "kernels.hpp"
@@ -44,12 +49,16 @@ constexpr int kRopeB = kKT * kDR * 2;                            // 4096
 constexpr int kStageB = kLatB + kRopeB;                          // 37376
 constexpr int kPB = kHMAX * kKT * 2;                             // P tile: 8192
 constexpr int kLdsB = kNS * kStageB + 2 * kPB + 2 * kHMAX * 4;
+constexpr int kMaxSparseChunk = 2048;                            // list entries staged per workgroup
 }  // namespace
 
+// SPARSE = false: sequence b's rows are 0 .. seq_lens[b]-1 (indices unused).
+// SPARSE = true:  its rows are indices[b, 0 .. topk-1] (seq_lens unused).
+template <bool SPARSE>
 __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
     const bf16* __restrict__ Qa, const bf16* __restrict__ KV, const int32_t* __restrict__ seq_lens,
-    float* __restrict__ part_o, float* __restrict__ part_ml, int H, int max_len, int chunk, int n_split,
-    float scale_log2) {
+    const int32_t* __restrict__ indices, float* __restrict__ part_o, float* __restrict__ part_ml, int H,
+    int max_len, int topk, int chunk, int n_split, float scale_log2) {
     constexpr int KS = kDK / 16;         // 36 score steps
     constexpr int KS_LAT = kDC / 16;     // 32 of them over the latent
     constexpr int MT = kDW / 32;         // 4 O^T M-tiles (value dims) per wave
@@ -57,16 +66,36 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
     constexpr int PF = 4;                // operand read-ahead
 
     __shared__ __attribute__((aligned(16))) char smem[kLdsB];
+    __shared__ int sidx[SPARSE ? kMaxSparseChunk : 1];          // this chunk's rows (-1: skipped)
     char* const pbuf = smem + kNS * kStageB;                    // [2][kPB]
     float* const alpha_buf = (float*)(pbuf + 2 * kPB);          // [2][kHMAX]
 
     const int s_idx = blockIdx.x;
     const int b = blockIdx.y;
-    const int L = min(max(seq_lens[b], 0), max_len);
+    // positions begin .. end-1 of the row list (cache rows, or list entries)
+    const int L = SPARSE ? topk : min(max(seq_lens[b], 0), max_len);
     const int begin = s_idx * chunk;
     if (begin >= L) return;
     const int end = min(begin + chunk, L);
     const int n_tiles = (end - begin + kKT - 1) / kKT;
+    if constexpr (SPARSE) {
+        const int32_t* ib = indices + (size_t)b * topk + begin;
+        for (int r = (int)threadIdx.x; r < end - begin; r += kNW * 64) {
+            const int v = ib[r];
+            sidx[r] = (v >= 0 && v < max_len) ? v : -1;
+        }
+        __syncthreads();
+    }
+    // cache row behind list position pos (begin <= pos < end); skipped
+    // entries read row 0 and are masked
+    auto cache_row = [&](int pos) -> int {
+        if constexpr (SPARSE) {
+            const int v = sidx[pos - begin];
+            return v < 0 ? 0 : v;
+        } else {
+            return pos;
+        }
+    };
 
     const int lane = lane_id();
     const int w = wave_id();
@@ -102,12 +131,14 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
         const int row0 = begin + tile * kKT;
         if (i < kKT / kNW) {
             const int u = i * kNW + w;               // wave-uniform latent row
-            const int key = min(row0 + u, end - 1);
-            copy16_to_lds_async_stream(KVb + (size_t)key * kDK, lane16, st + (uint32_t)(layout::mla_lat_pos(u) * kLatRowB));
+            const int key = cache_row(min(row0 + u, end - 1));
+            const uint32_t dst = st + (uint32_t)(layout::mla_lat_pos(u) * kLatRowB);
+            if constexpr (SPARSE) copy16_to_lds_async_stream(KVb, (uint32_t)key * (kDK * 2u) + lane16, dst);
+            else copy16_to_lds_async_stream(KVb + (size_t)key * kDK, lane16, dst);
         } else {
             const int r = 8 * w + (lane >> 3);       // RoPE row of this lane
             const int c = (lane & 7) ^ layout::mla_rope_swz(r);
-            const int key = min(row0 + r, end - 1);
+            const int key = cache_row(min(row0 + r, end - 1));
             copy16_to_lds_async_stream(KVb, (uint32_t)key * (kDK * 2u) + (uint32_t)(kDC * 2 + c * 16), st + (uint32_t)(kLatB + w * 1024));
         }
     };
@@ -182,7 +213,14 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
         // the scale folds into the exponent: p = 2^(s * c - m)
         const int row0 = begin + it * kKT;
         float mloc = -INFINITY;
-        if (row0 + kKT > end) {
+        if constexpr (SPARSE) {
+            // one validity bit per list entry of the tile (lane n: entry n)
+            const bool ok = row0 + n < end && sidx[min(row0 + n, end - 1) - begin] >= 0;
+            const uint32_t vm = (uint32_t)__ballot(ok);
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (!((vm >> (8 * (i >> 2) + 4 * h2 + (i & 3))) & 1u)) s[i] = -INFINITY;
+        } else if (row0 + kKT > end) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int key = row0 + 8 * (i >> 2) + 4 * h2 + (i & 3);
@@ -199,10 +237,13 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
             m_run = mnew;
             l_run *= alpha;
         }
+        // a sparse chunk can start with tiles of skipped entries only: then
+        // m_run is still -inf and every p must be 0 (2^(-inf - 0))
+        const float m_use = (SPARSE && m_run == -INFINITY) ? 0.f : m_run;
         float lsum = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            s[i] = fast_exp2(fmaf(s[i], scale_log2, -m_run));
+            s[i] = fast_exp2(fmaf(s[i], scale_log2, -m_use));
             lsum += s[i];
         }
         l_run += lsum;
@@ -312,15 +353,36 @@ DecodePlan mla_plan(int B, int max_len) {
     return p;
 }
 
+DecodePlan mla_sparse_plan(int B, int topk) {
+    // about 256 workgroups; 128 .. kMaxSparseChunk list entries each
+    const int target_wgs = 256;
+    int splits = (target_wgs + B - 1) / B;
+    int chunk = (topk + splits - 1) / splits;
+    if (chunk < 128) chunk = 128;
+    chunk = (chunk + kKT - 1) / kKT * kKT;
+    if (chunk > kMaxSparseChunk) chunk = kMaxSparseChunk;
+    DecodePlan p;
+    p.chunk = chunk;
+    p.n_split = (topk + chunk - 1) / chunk;
+    if (p.n_split < 1) p.n_split = 1;
+    return p;
+}
+
 hipError_t mla_launch(const MlaArgs& a) {
     const dim3 grid(a.plan.n_split, a.B);
-    hipLaunchKernelGGL(mla_decode_kernel, grid, dim3(kNW * 64), 0, a.stream, (const bf16*)a.q, (const bf16*)a.kv,
-                       a.seq_lens, a.part_o, a.part_ml, a.H, a.max_len, a.plan.chunk, a.plan.n_split,
-                       a.scale * kLog2e);
+    if (a.indices != nullptr)
+        hipLaunchKernelGGL(mla_decode_kernel<true>, grid, dim3(kNW * 64), 0, a.stream, (const bf16*)a.q,
+                           (const bf16*)a.kv, (const int32_t*)nullptr, a.indices, a.part_o, a.part_ml, a.H,
+                           a.max_len, a.topk, a.plan.chunk, a.plan.n_split, a.scale * kLog2e);
+    else
+        hipLaunchKernelGGL(mla_decode_kernel<false>, grid, dim3(kNW * 64), 0, a.stream, (const bf16*)a.q,
+                           (const bf16*)a.kv, a.seq_lens, (const int32_t*)nullptr, a.part_o, a.part_ml, a.H,
+                           a.max_len, 0, a.plan.chunk, a.plan.n_split, a.scale * kLog2e);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return merge_launch(a.part_o, a.part_ml, a.seq_lens, a.out, a.lse, a.B, a.H, a.max_len, kDC, a.plan.chunk,
-                        a.plan.n_split, a.out_f32, a.stream);
+    // sparse: every split of every sequence wrote a partial (seq_lens = null)
+    return merge_launch(a.part_o, a.part_ml, a.indices != nullptr ? nullptr : a.seq_lens, a.out, a.lse, a.B, a.H,
+                        a.max_len, kDC, a.plan.chunk, a.plan.n_split, a.out_f32, a.stream);
 }
 
 }  // namespace mqa

@@ -12,6 +12,7 @@ workload, inputs already resident in HBM:
                          T=8192, q/k 192 wide, v 128 wide
   * mqa_prefill_ex       chunked causal MQA prefill, B=2, Hq=16, Hkv=1,
                          d=512, 1024 new tokens after 7168 (bottom-right)
+  * mla_decode_sparse    batch 32, H=128, cache 32768, 2048 selected rows
 all bf16 in, fp32 accumulation, bf16 out.
 
 Every call is bracketed with HIP events on the stream it is launched on.
@@ -56,6 +57,7 @@ ORDER = (
     ("mla_decode_bf16_b32_l32768", "mla_decode"),
     ("mla_prefill_bf16_b1_h128_t8192", "mla_prefill"),
     ("mqa_chunk_prefill_bf16_b2_q1024_kv8192", "chunk_prefill"),
+    ("mla_sparse_decode_bf16_b32_l32768_k2048", "mla_sparse_decode"),
 )
 
 
@@ -184,7 +186,7 @@ def main():
 
     import torch
     import attention_mqa_gqa_amd as mqa
-    from synthetic import WORKLOADS, decode_inputs, mla_inputs, prefill_inputs
+    from synthetic import WORKLOADS, decode_inputs, draw_topk, mla_inputs, prefill_inputs
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -233,6 +235,21 @@ def main():
             work[name] = dict(flops=decode_flops(s["Hq"], s["D"], sl),
                               bytes=decode_bytes(s["B"], s["Hq"], s["Hkv"], s["D"], sl), bound="hbm", shape=s,
                               mean_len=float(np.mean(sl)))
+        elif wl.kind == "mla_sparse":
+            q, kv, sl = mla_inputs(s["B"], s["H"], s["L"], s["D"], "bf16", seed=0)
+            idx = draw_topk(s["B"], sl, s["topk"], seed=0)
+            dq, dkv, didx = to_dev(q), to_dev(kv), torch.from_numpy(idx).to(dev)
+            del kv
+            out = torch.empty((s["B"], s["H"], 512), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(mqa.mla_decode_sparse_workspace_size(s["B"], s["H"], s["topk"]), dtype=torch.uint8,
+                             device=dev)
+            sc = 192 ** -0.5
+            calls[name] = (lambda dq=dq, dkv=dkv, didx=didx, out=out, ws=ws, sc=sc:
+                           mqa.mla_decode_sparse(dq, dkv, didx, scale=sc, out=out, workspace=ws))
+            n_sel = (idx >= 0).sum(axis=1)              # rows read per sequence
+            work[name] = dict(flops=mla_flops(s["H"], s["D"], n_sel),
+                              bytes=mla_bytes(s["B"], s["H"], s["D"], n_sel) + idx.size * 4,
+                              bound="hbm", shape=s)
         else:
             q, kv, sl = mla_inputs(s["B"], s["H"], s["L"], s["D"], "bf16", seed=0)
             dq, dkv, dsl = to_dev(q), to_dev(kv), torch.from_numpy(sl).to(dev)

@@ -184,6 +184,32 @@ int mla_decode_absorbed(const void* q_abs, const void* kv_cache, const int32_t* 
                         int dtype, int out_dtype,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------- MLA sparse (top-k) decode
+ * Absorbed MLA decode over a selected subset of each sequence's cached rows:
+ * DeepSeek sparse attention keeps the MLA latent cache and lets each query
+ * attend only to the k positions an indexer selected (k = 2048 in V3.2;
+ * "带你了解Attention,从MHA到DeepSeek" (api.makesence.top) §5.1).  The
+ * selection is an input here (the indexer is not part of this library).
+ *   q_abs [B, H, 576]   kv_cache [B, max_len, 576]   out [B, H, 512]
+ *   indices int32 [B, topk] on the DEVICE: sequence b attends to the rows
+ *   kv_cache[b, indices[b, j]], j = 0 .. topk-1.  Entries outside
+ *   [0, max_len) are skipped (use -1 to pad sequences with fewer than topk
+ *   selected rows); they are never read.  The list normally names distinct
+ *   rows; a row listed twice enters the softmax twice.  A sequence with no
+ *   valid entry gets out = 0 and lse = -inf.
+ *   lse [B, H] fp32 or NULL.  scale as for mla_decode_absorbed.
+ * Supported: dtype BF16, out_dtype BF16 or F32, H a multiple of 16, H <= 128,
+ *   topk >= 1 (topk <= 0 is MQA_ERR_INVALID_ARG).
+ * Workspace: `mla_decode_sparse_workspace_size()` bytes (chunk partials of
+ *   the index list).
+ */
+size_t mla_decode_sparse_workspace_size(int B, int H, int topk);
+
+int mla_decode_sparse(const void* q_abs, const void* kv_cache, const int32_t* indices,
+                      void* out, float* lse, int B, int H, int max_len, int topk, float scale,
+                      int dtype, int out_dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }  /* extern "C" */
 #endif

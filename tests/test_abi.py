@@ -28,7 +28,7 @@ def _declared_functions():
 
 def test_header_functions_are_exported():
     names = _declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     assert sorted(names) == sorted(mqa.EXPORTED_SYMBOLS)
     for n in names:
         assert hasattr(lib, n), n
@@ -160,6 +160,26 @@ def test_mla_rejections():
     need = lib.mla_decode_workspace_size(32, 128, 32768)
     assert _mla(wsb=need - 1) == WORKSPACE
     assert _mla(B=0, q=None) == OK
+
+
+def _sparse(q=P, kv=P, idx=P, out=P, lse=None, B=32, H=128, L=32768, k=2048, scale=0.072, dt=BF16, dout=BF16,
+            ws=P, wsb=1 << 40):
+    return lib.mla_decode_sparse(q, kv, idx, out, lse, B, H, L, k, scale, dt, dout, ws, wsb, None)
+
+
+def test_mla_sparse_rejections():
+    assert _sparse(k=0) == INVALID
+    assert _sparse(L=0) == INVALID
+    assert _sparse(idx=None) == INVALID
+    assert _sparse(idx=ctypes.c_void_p(4098)) == INVALID
+    assert _sparse(scale=float("nan")) == INVALID
+    assert _sparse(H=24) == UNSUPPORTED
+    assert _sparse(dt=F32) == UNSUPPORTED
+    assert _sparse(ws=None) == WORKSPACE
+    need = lib.mla_decode_sparse_workspace_size(32, 128, 2048)
+    assert need > 0 and need % (32 * 128 * (512 + 2) * 4) == 0
+    assert _sparse(wsb=need - 1) == WORKSPACE
+    assert _sparse(B=0, q=None) == OK
 
 
 def test_decode_workspace_grows_with_splits():

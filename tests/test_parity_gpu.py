@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 from synthetic import (decode_inputs, decode_slice, mla_inputs, mla_slice, prefill_inputs,
-                       round_bf16, draw_lengths)
+                       round_bf16, draw_lengths, draw_topk)
 
 pytestmark = pytest.mark.gpu
 
@@ -353,6 +353,97 @@ def test_mla_full_size(torch, mqa):
     for b in (0, 31):
         qs, kvs = mla_slice(0, b, H, L)
         ref, ref_lse = oracle.mla_absorbed_ref(round_bf16(qs)[None], round_bf16(kvs)[None], np.array([L]), scale)
+        assert _maxerr(host(out[b]), ref[0]) <= BF16_TOL
+        assert _maxerr(host(lse[b]), ref_lse[0]) <= BF16_TOL
+
+
+# ---------------------------------------------------------------------------
+# sparse (top-k) MLA decode
+# ---------------------------------------------------------------------------
+
+def _sparse_check(torch, mqa, q, kv, idx, odt="bf16"):
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+    out_dtype = torch.float32 if odt == "f32" else torch.bfloat16
+    out = mqa.mla_decode_sparse(dev(torch, q), dev(torch, kv), torch.from_numpy(idx).cuda(), lse=lse,
+                                out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.mla_sparse_ref(q.f32(), kv.f32(), idx, 1 / math.sqrt(192))
+    got, got_lse = host(out), host(lse)
+    assert np.all(np.isfinite(got))
+    assert _maxerr(got, ref) <= BF16_TOL
+    empty = np.isinf(ref_lse)
+    assert np.array_equal(np.isinf(got_lse), empty)
+    if (~empty).any():
+        assert _maxerr(got_lse[~empty], ref_lse[~empty]) <= BF16_TOL
+    return out
+
+
+SPARSE_SMALL = [
+    # B, H, L_max, lengths, topk, out dtype
+    (3, 128, 5000, [5000, 3100, 500], 700, "bf16"),     # 500 < topk: -1 padding
+    (2, 64, 3000, None, 1000, "f32"),
+    (2, 16, 100, [100, 1], 1, "bf16"),
+    (1, 32, 40000, None, 2048, "bf16"),
+]
+
+
+@pytest.mark.parametrize("B,H,L,lengths,topk,odt", SPARSE_SMALL)
+def test_mla_sparse_small(torch, mqa, B, H, L, lengths, topk, odt):
+    _say(f"mla sparse B{B} H{H} L{L} lens={lengths} topk={topk} out={odt}")
+    q, kv, sl = mla_inputs(B, H, L, 576, "bf16", seed=10, lengths=lengths)
+    idx = draw_topk(B, sl, topk, seed=10)
+    _sparse_check(torch, mqa, q, kv, idx, odt)
+
+
+def test_mla_sparse_unsorted_duplicates_and_skips(torch, mqa):
+    """Unsorted lists, a repeated row, entries outside [0, L_max) (never
+    read), and a sequence that selects nothing (out 0, lse -inf)."""
+    _say("mla sparse irregular lists B3 H128 L900 topk 300")
+    B, H, L, k = 3, 128, 900, 300
+    q, kv, sl = mla_inputs(B, H, L, 576, "bf16", seed=11, lengths=[900, 900, 450])
+    rng = np.random.default_rng(11)
+    idx = np.full((B, k), -1, dtype=np.int32)
+    idx[0] = rng.permutation(900)[:k]                       # unsorted, distinct
+    idx[0, 17] = idx[0, 3]                                  # a repeated row
+    idx[0, 250:260] = [-1, 900, 5000, -7, 2 ** 30, -1, 899, 0, -2 ** 31, 12]
+    idx[1] = -1                                             # nothing selected
+    idx[2, :200] = rng.permutation(450)[:200]               # NaN rows >= 450 never listed
+    _sparse_check(torch, mqa, q, kv, idx)
+
+
+def test_mla_sparse_all_rows_equals_dense(torch, mqa):
+    """Listing rows 0..L_b-1 gives the dense absorbed decode (same kernel
+    arithmetic, different chunking)."""
+    _say("mla sparse vs dense B2 H128 L1500")
+    q, kv, sl = mla_inputs(2, 128, 1500, 576, "bf16", seed=12, lengths=[1500, 777])
+    idx = np.full((2, 1500), -1, dtype=np.int32)
+    for b in range(2):
+        idx[b, :sl[b]] = np.arange(sl[b])
+    sp = _sparse_check(torch, mqa, q, kv, idx)
+    de = mqa.mla_decode_absorbed(dev(torch, q), dev(torch, kv), torch.from_numpy(sl).cuda())
+    torch.cuda.synchronize()
+    assert _maxerr(host(sp), host(de)) <= BF16_TOL
+
+
+def test_mla_sparse_full_size(torch, mqa):
+    """Sparse MLA decode batch 32, H=128, cache 32768, 2048 selected rows per
+    sequence (the bench configuration); sampled sequences vs the oracle and
+    bitwise run-to-run repeatability."""
+    _say("mla sparse full B32 H128 L32768 topk 2048")
+    B, H, L, k = 32, 128, 32768, 2048
+    q, kv, sl = mla_inputs(B, H, L, 576, "bf16", seed=0)
+    idx = draw_topk(B, sl, k, seed=0)
+    dq, dkv, didx = dev(torch, q), dev(torch, kv), torch.from_numpy(idx).cuda()
+    del kv
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    out = mqa.mla_decode_sparse(dq, dkv, didx, lse=lse)
+    out2 = mqa.mla_decode_sparse(dq, dkv, didx)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    scale = 1 / math.sqrt(192)
+    for b in (0, 13, 31):
+        qs, kvs = mla_slice(0, b, H, L)
+        ref, ref_lse = oracle.mla_sparse_ref(round_bf16(qs)[None], round_bf16(kvs)[None], idx[b:b + 1], scale)
         assert _maxerr(host(out[b]), ref[0]) <= BF16_TOL
         assert _maxerr(host(lse[b]), ref_lse[0]) <= BF16_TOL
 
