@@ -37,6 +37,7 @@ __all__ = [
     "mla_decode_sparse_workspace_size",
     "DTYPE_F32",
     "DTYPE_BF16",
+    "DTYPE_F16",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -45,6 +46,7 @@ LIB_PATH = os.path.join(_PKG, "libmqa_attn.so")
 
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
+DTYPE_F16 = 2
 
 EXPORTED_SYMBOLS = (
     "mqa_attn_abi_version",
@@ -134,7 +136,9 @@ def _dtype_code(dt):
         return DTYPE_F32
     if dt == torch.bfloat16:
         return DTYPE_BF16
-    raise TypeError(f"unsupported dtype {dt}; use torch.float32 or torch.bfloat16")
+    if dt == torch.float16:
+        return DTYPE_F16
+    raise TypeError(f"unsupported dtype {dt}; use torch.float32, torch.bfloat16 or torch.float16")
 
 
 def _ptr(t):

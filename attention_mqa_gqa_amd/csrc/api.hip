@@ -13,9 +13,12 @@ using mqa::DecodePlan;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-bool valid_dtype(int d) { return d == MQA_DTYPE_F32 || d == MQA_DTYPE_BF16; }
+bool valid_dtype(int d) { return d == MQA_DTYPE_F32 || d == MQA_DTYPE_BF16 || d == MQA_DTYPE_F16; }
 
-size_t elem_bytes(int d) { return d == MQA_DTYPE_BF16 ? 2 : 4; }
+bool is16(int d) { return d == MQA_DTYPE_BF16 || d == MQA_DTYPE_F16; }
+
+// 16-bit inputs give their own type or fp32; fp32 inputs give fp32
+bool valid_out(int in, int out) { return out == MQA_DTYPE_F32 || (is16(in) && out == in); }
 
 thread_local hipError_t g_last_hip_error = hipSuccess;
 
@@ -62,7 +65,7 @@ const char* mqa_status_string(int status) {
 size_t mqa_prefill_ex_workspace_size(int B, int Hq, int Hkv, int T_q, int T_kv, int d_qk, int d_v, int in_dtype) {
     (void)Hq;
     (void)T_q;
-    if (in_dtype != MQA_DTYPE_BF16 || B <= 0 || Hkv <= 0 || T_kv <= 0 || d_qk <= 0 || d_v <= 0) return 0;
+    if (!is16(in_dtype) || B <= 0 || Hkv <= 0 || T_kv <= 0 || d_qk <= 0 || d_v <= 0) return 0;
     const mqa::PrefillPlan p = mqa::prefill_plan(d_qk, d_v, 1);
     if (p.kt <= 0) return 0;
     const size_t tiles = ((size_t)T_kv + p.kt - 1) / p.kt;
@@ -89,8 +92,8 @@ int mqa_prefill_ex(const void* q, const void* k, const void* v, void* out, float
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || (lse && ((uintptr_t)lse & 3u)))
         return MQA_ERR_INVALID_ARG;
     const int G = Hq / Hkv;
-    const bool bf = in_dtype == MQA_DTYPE_BF16;
-    if (!bf && out_dtype != MQA_DTYPE_F32) return MQA_ERR_UNSUPPORTED;
+    const bool bf = is16(in_dtype);
+    if (!valid_out(in_dtype, out_dtype)) return MQA_ERR_UNSUPPORTED;
     if (!prefill_supported(d_qk, d_v, G, bf)) return MQA_ERR_UNSUPPORTED;
     // the bf16 kernels address one (batch, KV head) tile stream with 32-bit
     // byte offsets
@@ -103,7 +106,8 @@ int mqa_prefill_ex(const void* q, const void* k, const void* v, void* out, float
     mqa::PrefillArgs a;
     a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
     a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Tq = T_q; a.Tkv = T_kv; a.DK = d_qk; a.DV = d_v; a.G = G;
-    a.scale = scale; a.causal = causal != 0; a.in_bf16 = bf; a.out_f32 = out_dtype == MQA_DTYPE_F32;
+    a.scale = scale; a.causal = causal != 0; a.in16 = bf; a.f16 = in_dtype == MQA_DTYPE_F16;
+    a.out_f32 = out_dtype == MQA_DTYPE_F32;
     a.workspace = workspace; a.stream = (hipStream_t)stream;
     clear_stale_error();
     return hip_status(mqa::prefill_launch(a));
@@ -134,7 +138,7 @@ int mqa_decode(const void* q, const void* k_cache, const void* v_cache, const in
         ((uintptr_t)seq_lens & 3u) || (lse && ((uintptr_t)lse & 3u)))
         return MQA_ERR_INVALID_ARG;
     const int G = Hq / Hkv;
-    if (dtype != MQA_DTYPE_BF16) return MQA_ERR_UNSUPPORTED;
+    if (!is16(dtype) || !valid_out(dtype, out_dtype)) return MQA_ERR_UNSUPPORTED;
     if (head_dim != 128 && head_dim != 512) return MQA_ERR_UNSUPPORTED;
     if (G > 16) return MQA_ERR_UNSUPPORTED;
     if (max_len == 0) return MQA_ERR_INVALID_ARG;  // a cache with no rows cannot hold the current token
@@ -145,7 +149,7 @@ int mqa_decode(const void* q, const void* k_cache, const void* v_cache, const in
     mqa::DecodeArgs a;
     a.q = q; a.k = k_cache; a.v = v_cache; a.seq_lens = seq_lens; a.out = out; a.lse = lse;
     a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.max_len = max_len; a.D = head_dim; a.G = G;
-    a.scale = scale; a.out_f32 = out_dtype == MQA_DTYPE_F32;
+    a.scale = scale; a.f16 = dtype == MQA_DTYPE_F16; a.out_f32 = out_dtype == MQA_DTYPE_F32;
     a.part_o = (float*)workspace;
     a.part_ml = (float*)workspace + (size_t)B * Hq * plan.n_split * head_dim;
     a.plan = plan; a.stream = (hipStream_t)stream;
@@ -169,7 +173,7 @@ int mla_decode_absorbed(const void* q_abs, const void* kv_cache, const int32_t* 
     if (!aligned16(q_abs) || !aligned16(kv_cache) || !aligned16(out) || ((uintptr_t)seq_lens & 3u) ||
         (lse && ((uintptr_t)lse & 3u)))
         return MQA_ERR_INVALID_ARG;
-    if (dtype != MQA_DTYPE_BF16) return MQA_ERR_UNSUPPORTED;
+    if (dtype != MQA_DTYPE_BF16 || !valid_out(dtype, out_dtype)) return MQA_ERR_UNSUPPORTED;
     if (H % 16 != 0 || H > 128) return MQA_ERR_UNSUPPORTED;
     if (max_len == 0) return MQA_ERR_INVALID_ARG;
     // one sequence's latent cache is addressed with 32-bit byte offsets
@@ -204,7 +208,7 @@ int mla_decode_sparse(const void* q_abs, const void* kv_cache, const int32_t* in
     if (!aligned16(q_abs) || !aligned16(kv_cache) || !aligned16(out) || ((uintptr_t)indices & 3u) ||
         (lse && ((uintptr_t)lse & 3u)))
         return MQA_ERR_INVALID_ARG;
-    if (dtype != MQA_DTYPE_BF16) return MQA_ERR_UNSUPPORTED;
+    if (dtype != MQA_DTYPE_BF16 || !valid_out(dtype, out_dtype)) return MQA_ERR_UNSUPPORTED;
     if (H % 16 != 0 || H > 128) return MQA_ERR_UNSUPPORTED;
     // one sequence's latent cache is addressed with 32-bit byte offsets
     if ((size_t)max_len * 576 * 2 > 0xFFFFFFFFull) return MQA_ERR_UNSUPPORTED;

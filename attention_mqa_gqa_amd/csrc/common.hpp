@@ -1,5 +1,12 @@
 // Device helpers shared by the gfx950 attention kernels: vector types, MFMA
-// wrappers, bf16 packing, wave reductions and the direct global->LDS copy.
+// wrappers, bf16 / fp16 packing, wave reductions and the direct global->LDS
+// copy.
+//
+// 16-bit element types: the kernels carry 16-bit operands as bit containers
+// (bf16x8, u32x4, u32x2) whatever the element type; only the MFMA opcode and
+// the fp32 -> 16-bit rounding depend on it.  Kernels templated on
+// `bool F16` read IEEE half inputs when F16 is true and bfloat16 otherwise,
+// through the *_t<F16> wrappers below.
 //
 // MFMA lane layouts used throughout (wave64, 16x16 output tiles):
 //   C/D  (f32x4): lane l holds C[4*(l/16) + i][l % 16], i = 0..3.
@@ -85,6 +92,43 @@ __device__ __forceinline__ f32x4 mfma_16x16x16(const u32x2& a, const u32x2& b, c
                                                      __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
 }
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// The MFMAs above for either 16-bit element type (operands as bit containers).
+template <bool F16>
+__device__ __forceinline__ f32x16 mfma_32x32x16_t(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    if constexpr (F16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                      0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+template <bool F16>
+__device__ __forceinline__ void mfma_32x32x16_acc_t(const bf16x8& a, const bf16x8& b, f32x16& acc) {
+    if constexpr (F16)
+        asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    else
+        asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+template <bool F16>
+__device__ __forceinline__ f32x4 mfma_16x16x32_t(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    if constexpr (F16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                      0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+template <bool F16>
+__device__ __forceinline__ f32x4 mfma_16x16x16_t(const u32x2& a, const u32x2& b, const f32x4& c) {
+    if constexpr (F16)
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c, 0,
+                                                     0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b),
+                                                         c, 0, 0, 0);
+}
+
 __device__ __forceinline__ f32x4 mfma_16x16x4_f32(float a, float b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
@@ -105,6 +149,27 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(const f32x4& lo, const f32x4& hi) 
     u.y = pack_bf16x2(lo.z, lo.w);
     u.z = pack_bf16x2(hi.x, hi.y);
     u.w = pack_bf16x2(hi.z, hi.w);
+    return __builtin_bit_cast(bf16x8, u);
+}
+
+// two floats -> two IEEE halves (round to nearest even)
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), f16x2));
+}
+template <bool F16>
+__device__ __forceinline__ uint32_t pack2_t(float lo, float hi) {
+    if constexpr (F16) return pack_f16x2(lo, hi);
+    else return pack_bf16x2(lo, hi);
+}
+template <bool F16>
+__device__ __forceinline__ bf16x8 pack8_t(const f32x4& lo, const f32x4& hi) {
+    u32x4 u;
+    u.x = pack2_t<F16>(lo.x, lo.y);
+    u.y = pack2_t<F16>(lo.z, lo.w);
+    u.z = pack2_t<F16>(hi.x, hi.y);
+    u.w = pack2_t<F16>(hi.z, hi.w);
     return __builtin_bit_cast(bf16x8, u);
 }
 

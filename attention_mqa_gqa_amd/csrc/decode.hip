@@ -18,6 +18,7 @@
 //     order, so the result is deterministic (no float atomics; lzwjava §4
 //     on ordering and determinism).
 // The cache streams with non-temporal loads (each row is read once).
+// F16: fp16 inputs (the _f16 MFMAs, P rounded to fp16); else bf16.
 // Cache rows at or beyond seq_lens[b] are never read.
 #include "common.hpp"
 #include "layout.hpp"
@@ -25,7 +26,7 @@
 
 namespace mqa {
 
-template <int D, int KSUB, int NW>
+template <int D, int KSUB, int NW, bool F16>
 __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(
     const bf16* __restrict__ Qp, const bf16* __restrict__ Kc, const bf16* __restrict__ Vc,
     const int32_t* __restrict__ seq_lens, float* __restrict__ part_o, float* __restrict__ part_ml, int Hq,
@@ -118,7 +119,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(
         for (int sub = 0; sub < KSUB; ++sub) {
             s[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) s[sub] = mfma_16x16x32(ka[sub][ks], qb[ks], s[sub]);
+            for (int ks = 0; ks < KS; ++ks) s[sub] = mfma_16x16x32_t<F16>(ka[sub][ks], qb[ks], s[sub]);
         }
         if (more) load_k(k0 + STEP);
         float mloc = -INFINITY;
@@ -150,8 +151,8 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(
                 p[i] = fast_exp2(s[sub][i] - m_run);
                 l_run += p[i];
             }
-            pb.x = pack_bf16x2(p[0], p[1]);
-            pb.y = pack_bf16x2(p[2], p[3]);
+            pb.x = pack2_t<F16>(p[0], p[1]);
+            pb.y = pack2_t<F16>(p[2], p[3]);
             // V^T operands: M-tile (sl, t): row n <-> head dim 128 sl + 8 n + t,
             // slot j <-> key 4g + j.
 #pragma unroll
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(
                     u32x2 a;
                     a.x = perm(vr[sub][sl][1][wd], vr[sub][sl][0][wd], sel);
                     a.y = perm(vr[sub][sl][3][wd], vr[sub][sl][2][wd], sel);
-                    o[sl * 8 + t] = mfma_16x16x16(a, pb, o[sl * 8 + t]);
+                    o[sl * 8 + t] = mfma_16x16x16_t<F16>(a, pb, o[sl * 8 + t]);
                 }
             }
         }
@@ -208,9 +209,10 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(
 // ---------------------------------------------------------------------------
 // LSE merge: out[b,h] = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M),
 // lse = M ln2 + ln(sum).  Splits are visited in index order.  One block per
-// (head, sequence); DV/4 threads with four head dims each.
+// (head, sequence); DV/4 threads with four head dims each.  Output fp32, or
+// 16-bit (fp16 if OUT_F16, else bf16).
 // ---------------------------------------------------------------------------
-template <int DV, bool OUT_F32>
+template <int DV, bool OUT_F32, bool OUT_F16>
 __global__ __launch_bounds__(DV / 4) void lse_merge_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml,
                                                            const int32_t* __restrict__ seq_lens, void* __restrict__ Out,
@@ -243,29 +245,31 @@ __global__ __launch_bounds__(DV / 4) void lse_merge_kernel(const float* __restri
         *(f32x4*)((float*)Out + row * DV + d4) = acc;
     } else {
         u32x2 pk;
-        pk.x = pack_bf16x2(acc.x, acc.y);
-        pk.y = pack_bf16x2(acc.z, acc.w);
+        pk.x = pack2_t<OUT_F16>(acc.x, acc.y);
+        pk.y = pack2_t<OUT_F16>(acc.z, acc.w);
         *(u32x2*)((bf16*)Out + row * DV + d4) = pk;
     }
     if (Lse != nullptr && threadIdx.x == 0) Lse[row] = lsum > 0.f ? M * kLn2 + __logf(lsum) : -INFINITY;
 }
 
 hipError_t merge_launch(const float* part_o, const float* part_ml, const int32_t* seq_lens, void* out, float* lse,
-                        int B, int H, int max_len, int D, int chunk, int n_split, bool out_f32, hipStream_t stream) {
+                        int B, int H, int max_len, int D, int chunk, int n_split, bool out_f32, bool out_f16,
+                        hipStream_t stream) {
     const dim3 grid(H, B);
+#define MQA_MERGE_ONE(DV, F32, F16)                                                                        \
+    hipLaunchKernelGGL((lse_merge_kernel<DV, F32, F16>), grid, dim3(DV / 4), 0, stream, part_o, part_ml,   \
+                       seq_lens, out, lse, H, max_len, chunk, n_split)
 #define MQA_MERGE(DV)                                                                                      \
     do {                                                                                                    \
-        if (out_f32)                                                                                        \
-            hipLaunchKernelGGL((lse_merge_kernel<DV, true>), grid, dim3(DV / 4), 0, stream, part_o, part_ml,  \
-                               seq_lens, out, lse, H, max_len, chunk, n_split);                              \
-        else                                                                                                \
-            hipLaunchKernelGGL((lse_merge_kernel<DV, false>), grid, dim3(DV / 4), 0, stream, part_o, part_ml, \
-                               seq_lens, out, lse, H, max_len, chunk, n_split);                              \
+        if (out_f32) MQA_MERGE_ONE(DV, true, false);                                                        \
+        else if (out_f16) MQA_MERGE_ONE(DV, false, true);                                                   \
+        else MQA_MERGE_ONE(DV, false, false);                                                               \
     } while (0)
     if (D == 512) MQA_MERGE(512);
     else if (D == 128) MQA_MERGE(128);
     else return hipErrorInvalidValue;
 #undef MQA_MERGE
+#undef MQA_MERGE_ONE
     return hipGetLastError();
 }
 
@@ -296,21 +300,22 @@ DecodePlan decode_plan(int B, int Hkv, int max_len, int head_dim) {
 hipError_t decode_launch(const DecodeArgs& a) {
     const float sl2 = a.scale * kLog2e;
     const dim3 grid(a.plan.n_split, a.Hkv, a.B);
+#define MQA_DECODE(D, KSUB, F16)                                                                              \
+    hipLaunchKernelGGL((decode_split_kernel<D, KSUB, 4, F16>), grid, dim3(256), 0, a.stream, (const bf16*)a.q,    \
+                       (const bf16*)a.k, (const bf16*)a.v, a.seq_lens, a.part_o, a.part_ml, a.Hq, a.Hkv, a.max_len, \
+                       a.G, a.plan.chunk, a.plan.n_split, sl2)
     if (a.D == 512) {
-        hipLaunchKernelGGL((decode_split_kernel<512, 1, 4>), grid, dim3(256), 0, a.stream, (const bf16*)a.q,
-                           (const bf16*)a.k, (const bf16*)a.v, a.seq_lens, a.part_o, a.part_ml, a.Hq, a.Hkv,
-                           a.max_len, a.G, a.plan.chunk, a.plan.n_split, sl2);
+        if (a.f16) MQA_DECODE(512, 1, true); else MQA_DECODE(512, 1, false);
     } else if (a.D == 128) {
-        hipLaunchKernelGGL((decode_split_kernel<128, 4, 4>), grid, dim3(256), 0, a.stream, (const bf16*)a.q,
-                           (const bf16*)a.k, (const bf16*)a.v, a.seq_lens, a.part_o, a.part_ml, a.Hq, a.Hkv,
-                           a.max_len, a.G, a.plan.chunk, a.plan.n_split, sl2);
+        if (a.f16) MQA_DECODE(128, 4, true); else MQA_DECODE(128, 4, false);
     } else {
         return hipErrorInvalidValue;
     }
+#undef MQA_DECODE
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return merge_launch(a.part_o, a.part_ml, a.seq_lens, a.out, a.lse, a.B, a.Hq, a.max_len, a.D, a.plan.chunk,
-                        a.plan.n_split, a.out_f32, a.stream);
+                        a.plan.n_split, a.out_f32, a.f16, a.stream);
 }
 
 }  // namespace mqa

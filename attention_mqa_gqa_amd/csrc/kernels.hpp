@@ -20,7 +20,8 @@ struct PrefillArgs {
     int G;
     float scale;
     bool causal;
-    bool in_bf16;
+    bool in16;        // 16-bit inputs (MFMA path); false: fp32 inputs
+    bool f16;         // 16-bit type is fp16 (else bf16); also the 16-bit output type
     bool out_f32;
     void* workspace;
     hipStream_t stream;
@@ -31,7 +32,7 @@ struct PrefillPlan {
     int kt;           // keys per K/V tile, bf16 path
 };
 
-PrefillPlan prefill_plan(int d_qk, int d_v, int in_bf16);
+PrefillPlan prefill_plan(int d_qk, int d_v, int in16);
 hipError_t prefill_launch(const PrefillArgs& a);
 
 // Split-KV decode plan shared by the workspace query and the launch.
@@ -53,6 +54,7 @@ struct DecodeArgs {
     float* lse;
     int B, Hq, Hkv, max_len, D, G;
     float scale;
+    bool f16;        // fp16 inputs and 16-bit output (else bf16)
     bool out_f32;
     float* part_o;   // [B*Hq*n_split, D]
     float* part_ml;  // [B*Hq*n_split, 2]
@@ -84,6 +86,6 @@ hipError_t mla_launch(const MlaArgs& a);
 // LSE merge of split partials (shared by both decode paths).
 hipError_t merge_launch(const float* part_o, const float* part_ml, const int32_t* seq_lens, void* out,
                         float* lse, int B, int H, int max_len, int D, int chunk, int n_split, bool out_f32,
-                        hipStream_t stream);
+                        bool out_f16, hipStream_t stream);
 
 }  // namespace mqa

@@ -382,7 +382,7 @@ hipError_t mla_launch(const MlaArgs& a) {
     if (e != hipSuccess) return e;
     // sparse: every split of every sequence wrote a partial (seq_lens = null)
     return merge_launch(a.part_o, a.part_ml, a.indices != nullptr ? nullptr : a.seq_lens, a.out, a.lse, a.B, a.H,
-                        a.max_len, kDC, a.plan.chunk, a.plan.n_split, a.out_f32, a.stream);
+                        a.max_len, kDC, a.plan.chunk, a.plan.n_split, a.out_f32, false, a.stream);
 }
 
 }  // namespace mqa

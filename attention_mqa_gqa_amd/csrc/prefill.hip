@@ -1,6 +1,7 @@
 // Causal / full prefill attention for query heads sharing key/value heads.
 //
-// bf16 path (flash-style, one pass over K/V, scores never materialised --
+// 16-bit path, bf16 or fp16 inputs (flash-style, one pass over K/V, scores
+// never materialised --
 // the tiling idea of "GQA和MLA详解" (lzwjava.github.io) §4 applied to the
 // (T,T) score matrix as that page's §1 describes):
 //   * one workgroup = one (batch, KV head) and a block of query tokens for
@@ -93,7 +94,8 @@ __global__ __launch_bounds__(256) void kv_pack_kernel(const bf16* __restrict__ K
 }
 
 // ---------------------------------------------------------------------------
-// bf16 flash prefill on v_mfma_f32_32x32x16_bf16.
+// 16-bit flash prefill on v_mfma_f32_32x32x16_bf16 (F16: _f16, fp16 inputs,
+// P and a 16-bit output rounded to fp16).
 //   DK  query/key width (128, 192 or 512)   DV  value width (128 or 512)
 //   NR  32-row N-tiles per wave             NW  waves per workgroup
 //   KT  keys per tile (32)
@@ -104,7 +106,7 @@ __global__ __launch_bounds__(256) void kv_pack_kernel(const bf16* __restrict__ K
 // score accumulators are the P operands of the P.V MFMA as they stand.
 // Causal: query token i (of Tq) sees keys j <= i + q_off, q_off = Tkv - Tq.
 // ---------------------------------------------------------------------------
-template <int DK, int DV, int NR, int NW, int KT, bool CAUSAL, bool OUT_F32>
+template <int DK, int DV, int NR, int NW, int KT, bool CAUSAL, bool OUT_F32, bool F16>
 __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ KVt,
     void* __restrict__ Out, float* __restrict__ Lse, int Hq, int Hkv, int Tq, int Tkv, int q_off,
@@ -294,7 +296,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
             const bf16x8 a = abuf[ks % PF];
             if (ks + PF < KS) abuf[ks % PF] = kread(kst, ks + PF);
 #pragma unroll
-            for (int nt = 0; nt < NR; ++nt) acc[nt] = mfma_32x32x16(a, qb[nt][ks], acc[nt]);
+            for (int nt = 0; nt < NR; ++nt) acc[nt] = mfma_32x32x16_t<F16>(a, qb[nt][ks], acc[nt]);
         }
     };
 
@@ -382,7 +384,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
                 const bf16x8 a = abuf[ks % PF];
                 if (ks + PF < KS) abuf[ks % PF] = kread(kst, ks + PF);
 #pragma unroll
-                for (int nt = 0; nt < NR; ++nt) sn[nt] = mfma_32x32x16(a, qb[nt][ks], sn[nt]);
+                for (int nt = 0; nt < NR; ++nt) sn[nt] = mfma_32x32x16_t<F16>(a, qb[nt][ks], sn[nt]);
 #pragma unroll
                 for (int i = ks * 16 / KS; i < (ks + 1) * 16 / KS; ++i) {
 #pragma unroll
@@ -404,7 +406,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
             for (int kp = 0; kp < KSP; ++kp) {
                 f32x4 lo = {sc[nt][8 * kp + 0], sc[nt][8 * kp + 1], sc[nt][8 * kp + 2], sc[nt][8 * kp + 3]};
                 f32x4 hi = {sc[nt][8 * kp + 4], sc[nt][8 * kp + 5], sc[nt][8 * kp + 6], sc[nt][8 * kp + 7]};
-                pb[nt][kp] = pack_bf16x8(lo, hi);
+                pb[nt][kp] = pack8_t<F16>(lo, hi);
                 // keeps the exponentials in phase A: without a use here the
                 // compiler sinks them past barrier B to the P.V MFMAs
                 asm volatile("" : "+v"(pb[nt][kp]));
@@ -440,7 +442,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
                 if (st + PF < NSTEP_PV) vbuf[st % PF] = *(const bf16x8*)vaddr(st + PF);
                 const int kp = st / MT_O, mt = st % MT_O;
 #pragma unroll
-                for (int nt = 0; nt < NR; ++nt) mfma_32x32x16_acc(a, pb[nt][kp], o[mt][nt]);
+                for (int nt = 0; nt < NR; ++nt) mfma_32x32x16_acc_t<F16>(a, pb[nt][kp], o[mt][nt]);
                 // two scores per max3
 #pragma unroll
                 for (int i = st * 8 / NSTEP_PV; i < (st + 1) * 8 / NSTEP_PV; ++i) {
@@ -499,7 +501,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
                     *(f32x4*)(dst + 4) = hi;
                 } else {
                     bf16* dst = (bf16*)Out + row * DV + d0;
-                    *(bf16x8*)dst = pack_bf16x8(lo, hi);
+                    *(bf16x8*)dst = pack8_t<F16>(lo, hi);
                 }
             }
         }
@@ -591,8 +593,8 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(const float* __restric
 // ---------------------------------------------------------------------------
 // Host-side launchers (validated arguments only).
 // ---------------------------------------------------------------------------
-template <int DK, int DV, int NR, int NW, int KT>
-static hipError_t launch_bf16(const PrefillArgs& a) {
+template <int DK, int DV, int NR, int NW, int KT, bool F16>
+static hipError_t launch_16(const PrefillArgs& a) {
     const int R = NW * 32 * NR;
     const int tok = R / a.G;
     const int n_tok_blocks = (a.Tq + tok - 1) / tok;
@@ -606,7 +608,7 @@ static hipError_t launch_bf16(const PrefillArgs& a) {
     const int P = a.B * a.Hkv;
     const int xcd_map = P % kNumXcd == 0 ? 1 : (kNumXcd % P == 0 && n_tok_blocks % (kNumXcd / P) == 0 ? 2 : 0);
 #define MQA_PREFILL_LAUNCH(C, F)                                                                              \
-    hipLaunchKernelGGL((prefill_bf16_kernel<DK, DV, NR, NW, KT, C, F>), grid, dim3(NW * 64), 0, a.stream,    \
+    hipLaunchKernelGGL((prefill_bf16_kernel<DK, DV, NR, NW, KT, C, F, F16>), grid, dim3(NW * 64), 0, a.stream, \
                        (const bf16*)a.q, (const bf16*)kvt, a.out, a.lse, a.Hq, a.Hkv, a.Tq, a.Tkv, q_off, a.G, \
                        tok, n_tok_blocks, n_kv_tiles, xcd_map, sl2)
     if (a.causal) {
@@ -635,9 +637,14 @@ static hipError_t launch_f32(const PrefillArgs& a) {
     return hipGetLastError();
 }
 
-PrefillPlan prefill_plan(int d_qk, int d_v, int in_bf16) {
+template <int DK, int DV, int NR, int NW, int KT>
+static hipError_t launch_bf16(const PrefillArgs& a) {
+    return a.f16 ? launch_16<DK, DV, NR, NW, KT, true>(a) : launch_16<DK, DV, NR, NW, KT, false>(a);
+}
+
+PrefillPlan prefill_plan(int d_qk, int d_v, int in16) {
     PrefillPlan p{};
-    if (!in_bf16) {
+    if (!in16) {
         // fp32: equal widths (multiples of 64 up to 512) or the 192 / 128 pair
         const bool ok = d_qk % 64 == 0 && d_v % 64 == 0 && d_qk <= 512 && d_v <= 512 &&
                         (d_qk == d_v || (d_qk == 192 && d_v == 128));
@@ -652,7 +659,7 @@ PrefillPlan prefill_plan(int d_qk, int d_v, int in_bf16) {
 }
 
 hipError_t prefill_launch(const PrefillArgs& a) {
-    if (!a.in_bf16) {
+    if (!a.in16) {
         if (a.DK == 192 && a.DV == 128) return launch_f32<192, 128>(a);
         if (a.DK != a.DV) return hipErrorInvalidValue;
         switch (a.DK) {

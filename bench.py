@@ -13,7 +13,8 @@ workload, inputs already resident in HBM:
   * mqa_prefill_ex       chunked causal MQA prefill, B=2, Hq=16, Hkv=1,
                          d=512, 1024 new tokens after 7168 (bottom-right)
   * mla_decode_sparse    batch 32, H=128, cache 32768, 2048 selected rows
-all bf16 in, fp32 accumulation, bf16 out.
+  * mqa_prefill          the first workload with fp16 inputs and output
+all bf16 in (but the last), fp32 accumulation, 16-bit out.
 
 Every call is bracketed with HIP events on the stream it is launched on.
 The headline `value` is the causal MQA prefill TFLOP/s (visible query/key
@@ -58,6 +59,7 @@ ORDER = (
     ("mla_prefill_bf16_b1_h128_t8192", "mla_prefill"),
     ("mqa_chunk_prefill_bf16_b2_q1024_kv8192", "chunk_prefill"),
     ("mla_sparse_decode_bf16_b32_l32768_k2048", "mla_sparse_decode"),
+    ("mqa_prefill_f16_b2_t4096", "f16_prefill"),
 )
 
 
@@ -205,9 +207,9 @@ def main():
         s = dict(wl.shape)
         if wl.kind == "prefill":
             T_kv, DV = s.get("T_kv", s["T"]), s.get("DV", s["D"])
-            q, k, v = prefill_inputs(s["B"], s["Hq"], s["Hkv"], s["T"], s["D"], "bf16", seed=0, d_v=DV, T_kv=T_kv)
+            q, k, v = prefill_inputs(s["B"], s["Hq"], s["Hkv"], s["T"], s["D"], wl.dtype, seed=0, d_v=DV, T_kv=T_kv)
             dq, dk, dv = to_dev(q), to_dev(k), to_dev(v)
-            out = torch.empty((s["B"], s["Hq"], s["T"], DV), dtype=torch.bfloat16, device=dev)
+            out = torch.empty((s["B"], s["Hq"], s["T"], DV), dtype=dq.dtype, device=dev)
             ws = torch.empty(max(1, mqa.mqa_prefill_ex_workspace_size(s["B"], s["Hq"], s["Hkv"], s["T"], T_kv, s["D"],
                                                                       DV, mqa.DTYPE_BF16)),
                              dtype=torch.uint8, device=dev)
@@ -294,7 +296,7 @@ def main():
         tflops = w["flops"] / (mean * 1e-3) / 1e12
         gbs = w["bytes"] / (mean * 1e-3) / 1e9
         tr = traffic.get(name)
-        r = {"workload": name, "shape": {k: v for k, v in w["shape"].items()},
+        r = {"workload": name, "dtype": WORKLOADS[name].dtype, "shape": {k: v for k, v in w["shape"].items()},
              "ms": {"mean": round(mean, 4), "median": round(float(np.median(ms)), 4), "min": round(float(ms.min()), 4)},
              "algorithmic_flops": w["flops"], "algorithmic_bytes": w["bytes"],
              "tflops": round(tflops, 2), "gbs": round(gbs, 1)}

@@ -25,10 +25,13 @@
  *     allocates nothing, keeps no state between calls, never synchronises,
  *     and enqueues its kernels on `stream` (a hipStream_t; NULL = the default
  *     stream).  Inputs are read-only; outputs and workspace are overwritten.
- *   - Element types: MQA_DTYPE_F32 (IEEE float) or MQA_DTYPE_BF16 (bfloat16).
- *     Products accumulate in fp32.  Probabilities are rounded to bf16 before
- *     the P.V product when the inputs are bf16; fp32 inputs stay fp32 end to
- *     end.  Conversions to bf16 round to nearest even.
+ *   - Element types: MQA_DTYPE_F32 (IEEE float), MQA_DTYPE_BF16 (bfloat16)
+ *     or MQA_DTYPE_F16 (IEEE half; the zdabc.icu benchmark runs its MQA
+ *     operator in float16 on the GPU).  Products accumulate in fp32.
+ *     Probabilities are rounded to the input's 16-bit type before the P.V
+ *     product when the inputs are 16-bit; fp32 inputs stay fp32 end to end.
+ *     A 16-bit input gives a result of the same type or fp32 (out_dtype).
+ *     Conversions to 16 bits round to nearest even.
  *   - `lse` (optional, may be NULL) receives the natural-log log-sum-exp of
  *     the scaled, masked scores of each query row, in fp32.
  *   - Every argument is validated on the host before any HIP call; a rejected
@@ -49,11 +52,12 @@
 extern "C" {
 #endif
 
-#define MQA_ATTN_ABI_VERSION 2
+#define MQA_ATTN_ABI_VERSION 3
 
 typedef enum {
     MQA_DTYPE_F32 = 0,
-    MQA_DTYPE_BF16 = 1
+    MQA_DTYPE_BF16 = 1,
+    MQA_DTYPE_F16 = 2          /* IEEE half: prefill and decode only */
 } mqa_dtype;
 
 typedef enum {
@@ -84,11 +88,11 @@ const char* mqa_last_hip_error_name(void);
  *   aligned: query i is the token at position i).
  *   scale: the factor on Q.K^T, normally 1/sqrt(D).  Must be finite and > 0.
  * Supported: Hq % Hkv == 0;
- *   in_dtype BF16 -> out_dtype BF16 or F32, D in {128, 512}, and the group
+ *   in_dtype BF16 or F16 -> out_dtype the same or F32, D in {128, 512}, and the group
  *     size G = Hq/Hkv a power of two with G <= 128 (D=512) or G <= 256
  *     (D=128);
  *   in_dtype F32 -> out_dtype F32, D a multiple of 64 up to 512, any G.
- * Workspace: bf16 inputs need `mqa_prefill_workspace_size()` bytes, where the
+ * Workspace: 16-bit inputs need `mqa_prefill_workspace_size()` bytes, where the
  * library first writes K and a transposed V as one stream of 32-key tiles
  * (2 * B * Hkv * ceil(T/32) * 32 * D * 2 bytes); F32 needs none (workspace
  * may be NULL with workspace_bytes 0).
@@ -123,9 +127,9 @@ int mqa_prefill(const void* q, const void* k, const void* v, void* out, float* l
  *   expanded and decode absorbed; dimensions as in walkerchi.com "Full 路线"
  *   §四 4.2).
  * Supported: everything mqa_prefill supports (d_qk == d_v, as listed there),
- *   plus (d_qk, d_v) = (192, 128) with any G <= 256 (bf16) or any G (fp32).
+ *   plus (d_qk, d_v) = (192, 128) with any G <= 256 (16-bit) or any G (fp32).
  *   T_q == 0 or B == 0 is an empty call; T_kv == 0 with T_q > 0 is rejected.
- * Workspace (bf16): `mqa_prefill_ex_workspace_size()` bytes =
+ * Workspace (16-bit inputs): `mqa_prefill_ex_workspace_size()` bytes =
  *   B * Hkv * ceil(T_kv/32) * 32 * (d_qk + d_v) * 2; F32 needs none.
  * mqa_prefill(..., T, head_dim, ...) is exactly
  * mqa_prefill_ex(..., T, T, head_dim, head_dim, ...).
@@ -150,7 +154,7 @@ int mqa_prefill_ex(const void* q, const void* k, const void* v, void* out, float
  *   gets out = 0 and lse = -inf.  Rows at or beyond seq_lens[b] are never
  *   read.
  *   lse [B, Hq] fp32 or NULL.
- * Supported: dtype BF16, out_dtype BF16 or F32, D in {128, 512},
+ * Supported: dtype BF16 or F16, out_dtype the same or F32, D in {128, 512},
  *   G = Hq/Hkv <= 16.
  * Workspace: `mqa_decode_workspace_size()` bytes (chunk partials).
  */

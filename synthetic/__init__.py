@@ -14,8 +14,10 @@ Per-slice streams let a check regenerate one sequence of a multi-gigabyte
 cache without drawing the rest.  Cache rows at or beyond ``seq_lens[b]`` are
 NaN, so any out-of-range read poisons the result.
 
-bfloat16 tensors are kept as ``uint16`` bit patterns (what the device reads);
-``Tensor.f32()`` gives their exact float32 values (what the oracle reads).
+bfloat16 tensors are kept as ``uint16`` bit patterns (what the device reads),
+float16 tensors as numpy ``float16`` (numpy's float32 -> float16 conversion
+rounds to nearest even); ``Tensor.f32()`` gives their exact float32 values
+(what the oracle reads).
 """
 
 from __future__ import annotations
@@ -82,7 +84,7 @@ def round_bf16(x):
 @dataclass
 class Tensor:
     """One input: float32 values (``dtype == "f32"``) or bf16 bit patterns."""
-    data: np.ndarray              # float32 or uint16 (bf16 bits)
+    data: np.ndarray              # float32, uint16 (bf16 bits) or float16
     dtype: str = "f32"
 
     @property
@@ -92,6 +94,7 @@ class Tensor:
     def f32(self, index=...):
         """Exact float32 values of ``data[index]``."""
         part = self.data[index]
+        # (float16 -> float32 is exact)
         return bf16_to_f32(part) if self.dtype == "bf16" else np.asarray(part, dtype=np.float32)
 
 
@@ -102,17 +105,19 @@ def _draw(seed, tid, b, shape):
 def _store(shape, dtype):
     if dtype == "bf16":
         return np.empty(shape, dtype=np.uint16)
+    if dtype == "f16":
+        return np.empty(shape, dtype=np.float16)
     if dtype == "f32":
         return np.empty(shape, dtype=np.float32)
     raise ValueError(dtype)
 
 
 def _put(dst, idx, vals, dtype):
-    dst[idx] = bf16_bits(vals) if dtype == "bf16" else vals
+    dst[idx] = bf16_bits(vals) if dtype == "bf16" else vals      # float16 stores round to nearest even
 
 
 def _nan(dtype):
-    return _BF16_NAN if dtype == "bf16" else np.float32(np.nan)
+    return _BF16_NAN if dtype == "bf16" else (np.float16(np.nan) if dtype == "f16" else np.float32(np.nan))
 
 
 def prefill_slice(seed, tid, b, H, T, D):
@@ -237,6 +242,9 @@ WORKLOADS = {
                  dict(B=128, Hq=64, Hkv=8, L=16384, D=128, lengths=(1024, 16384))),
         Workload("mla_decode_bf16_b32_l32768", "mla", "bf16",
                  dict(B=32, H=128, L=32768, D=576)),
+        # the MQA prefill in fp16 (the zdabc.icu benchmark's GPU dtype)
+        Workload("mqa_prefill_f16_b2_t4096", "prefill", "f16",
+                 dict(B=2, Hq=16, Hkv=1, T=4096, D=512)),
         # sparse (top-k) MLA decode: 2048 selected rows of a 32768-row cache
         Workload("mla_sparse_decode_bf16_b32_l32768_k2048", "mla_sparse", "bf16",
                  dict(B=32, H=128, L=32768, D=576, topk=2048)),

@@ -15,7 +15,7 @@ mqa = pytest.importorskip("attention_mqa_gqa_amd")
 lib = mqa.lib
 
 OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
-F32, BF16 = 0, 1
+F32, BF16, F16 = 0, 1, 2
 P = ctypes.c_void_p(4096)          # a 16-byte aligned stand-in: never dereferenced on these paths
 MIS = ctypes.c_void_p(4096 + 8)    # misaligned
 
@@ -35,7 +35,7 @@ def test_header_functions_are_exported():
 
 
 def test_version_and_status_strings():
-    assert lib.mqa_attn_abi_version() == 2
+    assert lib.mqa_attn_abi_version() == 3
     for s in (OK, INVALID, UNSUPPORTED, WORKSPACE, -4, 7):
         assert lib.mqa_status_string(s)
     assert lib.mqa_last_hip_error_name() == b"hipSuccess"
@@ -62,6 +62,9 @@ def test_prefill_rejections():
     assert _prefill(D=256) == UNSUPPORTED                # bf16: D in {128, 512}
     assert _prefill(D=512, Hq=256, Hkv=1) == UNSUPPORTED  # group larger than a workgroup's rows
     assert _prefill(din=F32, dout=BF16) == UNSUPPORTED
+    assert _prefill(din=BF16, dout=F16) == UNSUPPORTED     # 16-bit out = the input type
+    assert _prefill(din=F16, dout=BF16) == UNSUPPORTED
+    assert _prefill(din=3) == INVALID
     assert _prefill(din=F32, dout=F32, D=100) == UNSUPPORTED
     assert _prefill(ws=None, wsb=0) == WORKSPACE
     need = lib.mqa_prefill_workspace_size(1, 16, 1, 128, 512, BF16)
@@ -72,6 +75,15 @@ def test_prefill_rejections():
 def test_prefill_empty_calls_are_ok():
     assert _prefill(B=0, q=None, k=None, v=None, out=None) == OK
     assert _prefill(T=0, q=None, k=None, v=None, out=None) == OK
+
+
+def test_f16_is_accepted_where_supported():
+    # validation passes up to the workspace check (no HIP call is made)
+    assert _prefill(din=F16, dout=F16, ws=None, wsb=0) == WORKSPACE
+    assert _prefill(din=F16, dout=F32, ws=None, wsb=0) == WORKSPACE
+    assert _decode(dt=F16, dout=F16, ws=None) == WORKSPACE
+    assert lib.mqa_prefill_workspace_size(2, 16, 1, 4096, 512, F16) == lib.mqa_prefill_workspace_size(
+        2, 16, 1, 4096, 512, BF16)
 
 
 def test_prefill_workspace_size():
@@ -135,6 +147,7 @@ def test_decode_rejections():
     assert _decode(L=0) == INVALID
     assert _decode(scale=0.0) == INVALID
     assert _decode(dt=F32, dout=F32) == UNSUPPORTED
+    assert _decode(dt=F16, dout=BF16) == UNSUPPORTED
     assert _decode(D=256) == UNSUPPORTED
     assert _decode(Hq=64, Hkv=2) == UNSUPPORTED          # group of 32 > 16 MFMA columns
     assert _decode(ws=None) == WORKSPACE
@@ -156,6 +169,8 @@ def test_mla_rejections():
     assert _mla(H=24) == UNSUPPORTED
     assert _mla(H=256) == UNSUPPORTED
     assert _mla(dt=F32) == UNSUPPORTED
+    assert _mla(dt=F16, dout=F16) == UNSUPPORTED          # MLA: bf16 only
+    assert _mla(dt=BF16, dout=F16) == UNSUPPORTED
     assert _mla(ws=None) == WORKSPACE
     need = lib.mla_decode_workspace_size(32, 128, 32768)
     assert _mla(wsb=need - 1) == WORKSPACE

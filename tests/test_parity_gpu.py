@@ -22,6 +22,9 @@ pytestmark = pytest.mark.gpu
 
 BF16_TOL = 2e-2
 F32_TOL = 1e-5
+# fp16 (10-bit mantissa; the bf16 bar's error budget scaled by the 8x finer
+# rounding of inputs, P and output, with margin)
+F16_TOL = 5e-3
 
 
 def _say(msg):
@@ -192,6 +195,34 @@ def test_prefill_ex_f32(torch, mqa, causal):
         assert _maxerr(host(lse), ref_lse) <= F32_TOL
 
 
+F16_CASES = [
+    # B, Hq, Hkv, T_q, T_kv, d_qk, d_v, causal, out dtype
+    (2, 16, 1, 200, 200, 512, 512, True, "f16"),
+    (1, 16, 1, 130, 333, 512, 512, True, "f32"),
+    (1, 64, 8, 150, 150, 128, 128, True, "f16"),
+    (1, 8, 8, 100, 300, 192, 128, True, "f16"),
+    (1, 12, 4, 65, 65, 128, 128, False, "f32"),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Tq,Tkv,DK,DV,causal,odt", F16_CASES)
+def test_prefill_f16(torch, mqa, B, Hq, Hkv, Tq, Tkv, DK, DV, causal, odt):
+    """fp16 inputs (the zdabc.icu benchmark's GPU dtype), fp16 or fp32 out."""
+    _say(f"prefill f16 B{B} Hq{Hq} Hkv{Hkv} Tq{Tq} Tkv{Tkv} DK{DK} DV{DV} causal={causal} out={odt}")
+    q, k, v = prefill_inputs(B, Hq, Hkv, Tq, DK, "f16", seed=7, d_v=DV, T_kv=Tkv)
+    lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device="cuda")
+    out_dtype = torch.float32 if odt == "f32" else torch.float16
+    fn = mqa.mqa_prefill if (Tq == Tkv and DK == DV) else mqa.mqa_prefill_ex
+    out = fn(dev(torch, q), dev(torch, k), dev(torch, v), causal=causal, lse=lse, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    assert out.dtype == out_dtype
+    ref, ref_lse = oracle.prefill_ref(q.f32(), k.f32(), v.f32(), 1 / math.sqrt(DK), causal)
+    err = _maxerr(host(out), ref)
+    _say(f"  max |err| {err:.2e}")
+    assert err <= F16_TOL
+    assert _maxerr(host(lse), ref_lse) <= F16_TOL
+
+
 def test_prefill_ex_square_matches_prefill(torch, mqa):
     """mqa_prefill_ex with T_q = T_kv and d_v = d_qk is the square entry point,
     bit for bit."""
@@ -355,6 +386,24 @@ def test_mla_full_size(torch, mqa):
         ref, ref_lse = oracle.mla_absorbed_ref(round_bf16(qs)[None], round_bf16(kvs)[None], np.array([L]), scale)
         assert _maxerr(host(out[b]), ref[0]) <= BF16_TOL
         assert _maxerr(host(lse[b]), ref_lse[0]) <= BF16_TOL
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,L,D,lengths,odt", [(4, 16, 1, 3000, 512, (1, 3000), "f16"),
+                                                      (8, 64, 8, 2500, 128, (1000, 2500), "f32")])
+def test_decode_f16(torch, mqa, B, Hq, Hkv, L, D, lengths, odt):
+    _say(f"decode f16 B{B} Hq{Hq} Hkv{Hkv} L{L} D{D} lens={lengths} out={odt}")
+    q, k, v, sl = decode_inputs(B, Hq, Hkv, L, D, "f16", seed=8, lengths=lengths)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    out_dtype = torch.float32 if odt == "f32" else torch.float16
+    out = mqa.mqa_decode(dev(torch, q), dev(torch, k), dev(torch, v), torch.from_numpy(sl).cuda(), lse=lse,
+                         out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    assert out.dtype == out_dtype
+    ref, ref_lse = oracle.decode_ref(q.f32(), k.f32(), v.f32(), sl, 1 / math.sqrt(D))
+    err = _maxerr(host(out), ref)
+    _say(f"  max |err| {err:.2e}")
+    assert err <= F16_TOL
+    assert _maxerr(host(lse), ref_lse) <= F16_TOL
 
 
 # ---------------------------------------------------------------------------
