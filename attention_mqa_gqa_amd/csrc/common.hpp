@@ -263,6 +263,24 @@ __device__ __forceinline__ void copy16_to_lds_async(const void* base, uint32_t v
         : "memory", "m0");
 }
 
+// Four 1 KB copies S bytes apart (global base + S k -> LDS lds_byte + S k,
+// k = 0..3) under one M0 write: the instruction offset moves both the
+// global and the LDS address.
+template <int S>
+__device__ __forceinline__ void copy4_to_lds_async(const void* base, uint32_t voff, uint32_t lds_byte) {
+    static_assert(S >= 1024 && 3 * S < 4096, "offset field");
+    asm volatile(
+        "s_nop 4\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %0, %1\n\t"
+        "global_load_lds_dwordx4 %0, %1 offset:%3\n\t"
+        "global_load_lds_dwordx4 %0, %1 offset:%4\n\t"
+        "global_load_lds_dwordx4 %0, %1 offset:%5"
+        :
+        : "v"(voff), "s"(base), "s"(lds_byte), "n"(S), "n"(2 * S), "n"(3 * S)
+        : "memory", "m0");
+}
+
 // Four consecutive 1 KB copies (global base + 1024 k -> LDS lds_byte +
 // 1024 k, k = 0..3) under one M0 write: the instruction offset moves both
 // the global and the LDS address.

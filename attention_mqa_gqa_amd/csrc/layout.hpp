@@ -94,6 +94,12 @@ MQA_HD constexpr int swz32_group(int row_chunks) { return row_chunks % 16 == 0 ?
 MQA_HD constexpr int padded_row_bytes(int row_bytes) { return row_bytes + 16; }
 MQA_HD constexpr int padded_row_pos(int key_row) { return swap23(key_row & 31) | (key_row & ~31); }
 
+// Bytes of one prefill K tile of kt keys as stored in the workspace tile
+// stream and in LDS: padded 1 KB rows (d_qk = 512) or plain swizzled rows.
+MQA_HD constexpr int prefill_k_tile_bytes(int kt, int d_qk) {
+    return 2 * d_qk == 1024 ? kt * padded_row_bytes(1024) : kt * 2 * d_qk;
+}
+
 // MLA-absorbed decode tiles (32 cache rows).
 // Latent rows (1 KB + 16 B padding): row k of the tile sits at row position
 // 8(k/8) + 2(k%4) + (k/4)%2.  Score reads (lane n reads row n) then hit

@@ -32,11 +32,11 @@ namespace mqa {
 // ---------------------------------------------------------------------------
 // K [B*Hkv, T, DK], V [B*Hkv, T, DV] -> tile stream
 // [B*Hkv, n_tiles, (K tile | V^T tile)].
-// Each 32-key tile is stored as the prefill kernel keeps it in LDS: the K
-// tile row-major (row = key; 16-byte chunks in swizzled order unless a row
-// is exactly one 1 KB copy, which the kernel places with padding instead)
-// and the V^T tile (row = value dim, 32 keys per row, swizzled chunks), zero
-// past T.  V's
+// Each 32-key tile is stored exactly as the prefill kernel keeps it in LDS:
+// the K tile row-major (row = key; 16-byte chunks in swizzled order, except
+// rows of exactly 1 KB, which are stored in plain order with 16 bytes of
+// padding, key layout::padded_row_pos(p) at row position p) and the V^T tile
+// (row = value dim, 32 keys per row, swizzled chunks), zero past T.  V's
 // contraction index (the key) is its row index, so the P.V operand needs it
 // transposed; doing that here once, and storing both tiles contiguously,
 // turns every global->LDS copy of the main kernel into a straight 16-byte
@@ -48,23 +48,25 @@ __global__ __launch_bounds__(256) void kv_pack_kernel(const bf16* __restrict__ K
     constexpr int RL = KT / 8;           // 16-byte chunks per V^T row
     constexpr int ROW_CHUNKS = DK / 8;   // 16-byte chunks per K row
     constexpr int NB = RL * (DV / 8);    // 8x8 blocks per V tile
-    constexpr int TILE_K = KT * DK;
+    constexpr bool KPAD = (2 * DK == 1024);
+    constexpr int KTILE_B = layout::prefill_k_tile_bytes(KT, DK);
+    constexpr int KROW_B = KTILE_B / KT;
     constexpr int TILE_V = KT * DV;
     const int tile = blockIdx.x;
     const size_t bh = blockIdx.y;
     const bf16* ksrc = K + bh * (size_t)T * DK;
     const bf16* vsrc = V + bh * (size_t)T * DV;
-    bf16* kdst = KVt + (bh * n_tiles + tile) * (size_t)(TILE_K + TILE_V);
-    bf16* vdst = kdst + TILE_K;
-    // K tile: chunk position p of row kk holds global chunk p ^ swz(kk)
-    // (plain order for 1 KB rows)
+    char* kdst = (char*)KVt + (bh * n_tiles + tile) * (size_t)(KTILE_B + 2 * TILE_V);
+    bf16* vdst = (bf16*)(kdst + KTILE_B);
+    // K tile: chunk position p of row position kk holds global chunk
+    // p ^ swz(kk) of key kk, or (1 KB rows) chunk p of key padded_row_pos(kk)
     for (int q = threadIdx.x; q < KT * ROW_CHUNKS; q += 256) {
         const int kk = q / ROW_CHUNKS;
         const int p = q % ROW_CHUNKS;
-        const int c = (2 * DK == 1024) ? p : (p ^ layout::swz32(kk, ROW_CHUNKS));
-        const int key = tile * KT + kk;
+        const int c = KPAD ? p : (p ^ layout::swz32(kk, ROW_CHUNKS));
+        const int key = tile * KT + (KPAD ? layout::padded_row_pos(kk) : kk);
         const u32x4 val = key < T ? ldg16(ksrc + (size_t)key * DK + c * 8) : u32x4{0, 0, 0, 0};
-        *(u32x4*)(kdst + (size_t)q * 8) = val;
+        *(u32x4*)(kdst + kk * KROW_B + p * 16) = val;
     }
     // V^T tile: 8x8 blocks transposed with byte permutes
     for (int blk = threadIdx.x; blk < NB; blk += 256) {
@@ -135,12 +137,12 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     // contraction step of its row from one address register plus an
     // immediate offset.  Narrower rows are swizzled instead.
     constexpr bool KPAD = (2 * DK == 1024);
-    constexpr int KROW_B = KPAD ? layout::padded_row_bytes(2 * DK) : 2 * DK;   // LDS bytes per K row
-    constexpr int KSTAGE_B = KT * KROW_B;                  // LDS bytes per K stage
+    constexpr int KSTAGE_B = layout::prefill_k_tile_bytes(KT, DK);   // LDS bytes per K stage
+    constexpr int KROW_B = KSTAGE_B / KT;                            // LDS bytes per K row
     constexpr int VSTAGE_B = 2 * TILE_V;                   // LDS bytes per V^T stage
     static_assert(KT == 32, "key tile");
     static_assert(CV % NW == 0, "V^T tile must split evenly over the waves");
-    static_assert((CK % NW) * 64 % NW == 0 && (!KPAD || PLK == 0), "K tile split");
+    static_assert((CK % NW) * 64 % NW == 0 && (!KPAD || (PLK == 0 && FK % 4 == 0)), "K tile split");
 
     __shared__ __attribute__((aligned(16))) char smem[2 * KSTAGE_B + 2 * VSTAGE_B];
 
@@ -205,7 +207,8 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     }
 
     const size_t bh = (size_t)b * Hkv + hk;
-    const bf16* KVbh = KVt + bh * (size_t)n_kv_tiles * (TILE_K + TILE_V);
+    constexpr int TILE_B = KSTAGE_B + 2 * TILE_V;      // bytes per tile in the stream
+    const char* KVbh = (const char*)KVt + bh * (size_t)n_kv_tiles * TILE_B;
 
     const int t_last = min(Tq, t0 + tok_per_wg) - 1;
     const int n_tiles = CAUSAL ? ((t_last + q_off) / KT + 1) : n_kv_tiles;
@@ -220,23 +223,32 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     const uint32_t lds_base = lds_addr(smem);
     const uint32_t lane16 = (uint32_t)lane * 16u;
     auto issue_k = [&](int tile) {
-        const bf16* src = KVbh + (size_t)tile * (TILE_K + TILE_V);
+        const char* src = KVbh + (size_t)tile * TILE_B;
         const uint32_t dst = lds_base + (uint32_t)((tile & 1) * KSTAGE_B);
+        if constexpr (KPAD) {
+            // padded 1 KB rows, identical in the stream and in LDS: runs of
+            // four rows, four copies per M0 write
 #pragma unroll
-        for (int i = 0; i < FK; ++i) {
-            const int inst = i * NW + w;               // wave-uniform
-            const uint32_t pos = KPAD ? (uint32_t)layout::padded_row_pos(inst) * KROW_B : (uint32_t)inst * 1024u;
-            copy16_to_lds_async(src + inst * 64 * 8, lane16, dst + pos);
+            for (int g = 0; g < FK / 4; ++g) {
+                const int row = (g * NW + w) * 4;
+                copy4_to_lds_async<KROW_B>(src + row * KROW_B, lane16, dst + (uint32_t)(row * KROW_B));
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < FK; ++i) {
+                const int inst = i * NW + w;               // wave-uniform
+                copy16_to_lds_async(src + inst * 1024, lane16, dst + (uint32_t)inst * 1024u);
+            }
         }
         if constexpr (PLK != 0) {
             // last round: wave w copies bytes [FK NW 1 KB + 16 PLK w, +16 PLK)
             // of the (unpadded) tile with its first PLK lanes
             const uint32_t off = (uint32_t)(FK * NW * 1024 + w * PLK * 16);
-            if (lane < PLK) copy16_to_lds_async((const char*)src + off, lane16, dst + off);
+            if (lane < PLK) copy16_to_lds_async(src + off, lane16, dst + off);
         }
     };
     auto issue_v = [&](int tile) {
-        const bf16* src = KVbh + (size_t)tile * (TILE_K + TILE_V) + TILE_K;
+        const char* src = KVbh + (size_t)tile * TILE_B + KSTAGE_B;
         const uint32_t dst = lds_base + (uint32_t)(2 * KSTAGE_B + (tile & 1) * VSTAGE_B);
         if constexpr (LHV % 4 == 0) {
             // V^T tiles are contiguous in both places: each wave copies runs of
@@ -244,13 +256,13 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
 #pragma unroll
             for (int g = 0; g < LHV / 4; ++g) {
                 const int inst = (g * NW + w) * 4;
-                copy4x1k_to_lds_async(src + inst * 64 * 8, lane16, dst + (uint32_t)inst * 1024u);
+                copy4x1k_to_lds_async(src + inst * 1024, lane16, dst + (uint32_t)inst * 1024u);
             }
         } else {
 #pragma unroll
             for (int i = 0; i < LHV; ++i) {
                 const int inst = i * NW + w;
-                copy16_to_lds_async(src + inst * 64 * 8, lane16, dst + (uint32_t)inst * 1024u);
+                copy16_to_lds_async(src + inst * 1024, lane16, dst + (uint32_t)inst * 1024u);
             }
         }
     };
