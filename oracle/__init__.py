@@ -18,6 +18,9 @@ be checked against the pages by eye.  Sources (page title, section):
   MQA operator, section "head_dim = 512 为什么值得注意"; makesence §3.1.
 * MLA latent cache, matrix absorption and decoupled RoPE key: lzwjava §3,
   makesence §4.3 and §4.5, walkerchi §四 4.2-4.3.
+* the steps around absorbed MLA decode -- query absorption, RoPE of the
+  decoupled part (``apply_rotary_pos_emb`` as walkerchi §四 4.2 calls it),
+  output up-projection: lzwjava §3, walkerchi §四 4.2-4.3.
 * MLA prefill in the expanded (MHA) form and decode in the absorbed form:
   makesence §4.4; sparse (top-k) attention over the MLA cache: makesence §5.1.
 * chunked prefill (queries = the last T of S tokens, bottom-right causal
@@ -39,4 +42,5 @@ from .attention_ref import (  # noqa: F401
     prefill_ref,
     prefill_rows_ref,
     repeat_kv_heads,
+    rope_ref,
 )

@@ -35,6 +35,7 @@ __all__ = [
     "lse_merge",
     "mla_absorbed_ref",
     "mla_sparse_ref",
+    "rope_ref",
     "absorb_query",
     "mla_explicit_ref",
     "kv_values_per_token",
@@ -262,6 +263,20 @@ def mla_sparse_ref(q_abs, kv_cache, indices, scale, d_v=512):
                        np.ones((H, len(sel)), dtype=bool))
         out[b], lse[b] = o, s
     return out, lse
+
+
+def rope_ref(x, cos, sin):
+    """Rotary position embedding of the decoupled RoPE part, in the form the
+    pages call (walkerchi §四 4.2: ``apply_rotary_pos_emb(q_rope, k_pe, cos,
+    sin)`` with ``cos, sin = position_embeddings``): with the last axis split
+    into halves x = [x1 | x2], rotate_half(x) = [-x2 | x1] and
+    RoPE(x) = x * cos + rotate_half(x) * sin.  cos and sin hold the rotary
+    factors of each row's position, broadcast over the leading axes.
+    """
+    x, cos, sin = _f64(x), _f64(cos), _f64(sin)
+    h = x.shape[-1] // 2
+    rot = np.concatenate([-x[..., h:], x[..., :h]], axis=-1)
+    return x * cos + rot * sin
 
 
 def absorb_query(q_nope, q_rope, w_uk):

@@ -51,6 +51,8 @@ __all__ = [
     "decode_inputs",
     "mla_inputs",
     "draw_topk",
+    "rope_tables",
+    "mla_step_inputs",
     "draw_lengths",
     "Workload",
     "WORKLOADS",
@@ -212,6 +214,31 @@ def draw_topk(B, seq_lens, topk, seed):
         sel = np.random.default_rng([seed, 98, b]).choice(L, size=n, replace=False)
         idx[b, :n] = np.sort(sel).astype(np.int32)
     return idx
+
+
+def rope_tables(positions, dim=64, base=10000.0):
+    """Rotary factors (cos, sin) float32 [n, dim] for integer positions, in
+    the usual table layout: inv_freq_i = base^(-2i/dim) for i < dim/2,
+    angle = position * inv_freq, and both halves of a row repeat the dim/2
+    angles.  (Kernel inputs, like a model's position embeddings.)"""
+    pos = np.asarray(positions, dtype=np.float64)[:, None]
+    inv = base ** (-np.arange(0, dim, 2, dtype=np.float64) / dim)
+    ang = np.concatenate([pos * inv, pos * inv], axis=1)
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def mla_step_inputs(B, H, dtype="bf16", seed=0, d_c=512, d_nope=128, d_r=64, d_v=128):
+    """One MLA decode step's inputs: q_nope [B,H,d_nope], q_rope [B,H,d_r],
+    the new token's c_kv [B,d_c] and k_pe [B,d_r] (before RoPE), and
+    per-head weights w_uk [H,d_c,d_nope], w_uv [H,d_c,d_v] drawn N(0,1) and
+    scaled by 1/sqrt(fan-in) (tensor ids 10..15)."""
+    def one(tid, shape, scale=1.0):
+        t = _store(shape, dtype)
+        _put(t, ..., np.random.default_rng([seed, tid]).standard_normal(shape, dtype=np.float32) * np.float32(scale),
+             dtype)
+        return Tensor(t, dtype)
+    return (one(10, (B, H, d_nope)), one(11, (B, H, d_r)), one(12, (B, d_c)), one(13, (B, d_r)),
+            one(14, (H, d_c, d_nope), 1 / np.sqrt(d_nope)), one(15, (H, d_c, d_v), 1 / np.sqrt(d_c)))
 
 
 def mla_slice(seed, b, H, L, d_kv=576):

@@ -14,7 +14,8 @@ import numpy as np
 import pytest
 
 import oracle
-from synthetic import prefill_inputs, decode_inputs, mla_inputs, draw_topk, round_bf16, bf16_bits, bf16_to_f32
+from synthetic import (prefill_inputs, decode_inputs, mla_inputs, draw_topk, rope_tables, round_bf16, bf16_bits,
+                       bf16_to_f32)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -477,6 +478,61 @@ def test_mla_ignores_padding_and_uses_leading_latent_as_value():
     a, _ = oracle.mla_absorbed_ref(qz, kv.f32(), lens, 0.5, d_v=8)
     b, _ = oracle.mla_absorbed_ref(qz, kv2, lens, 0.5, d_v=8)
     assert np.max(np.abs(a - b)) <= 1e-14
+
+
+# ---------------------------------------------------------------------------
+# RoPE of the decoupled part and the whole MLA decode step around the
+# absorbed attention.
+# ---------------------------------------------------------------------------
+
+def test_rope_special_angles():
+    x = np.arange(1.0, 9.0)                         # halves [1..4 | 5..8]
+    one, zero = np.ones(8), np.zeros(8)
+    assert np.array_equal(oracle.rope_ref(x, one, zero), x)                       # angle 0: identity
+    assert np.array_equal(oracle.rope_ref(x, zero, one), [-5, -6, -7, -8, 1, 2, 3, 4])   # quarter turn
+    assert np.array_equal(oracle.rope_ref(x, -one, zero), -x)                     # half turn
+
+
+def test_rope_is_a_rotation_by_position_difference():
+    """<RoPE(q, m), RoPE(k, n)> = <RoPE(q, m - n), k> for the standard tables
+    (angle addition: the score depends only on the relative position), and
+    every (i, i + 32) pair keeps its norm."""
+    rng = np.random.default_rng(40)
+    q, k = rng.standard_normal(64), rng.standard_normal(64)
+    for m, n in ((7, 3), (100, 0), (5, 9), (4096, 4000)):
+        c, s_ = rope_tables([m, n, m - n])
+        c, s_ = c.astype(np.float64), s_.astype(np.float64)
+        lhs = oracle.rope_ref(q, c[0], s_[0]) @ oracle.rope_ref(k, c[1], s_[1])
+        rhs = oracle.rope_ref(q, c[2], s_[2]) @ k
+        assert abs(lhs - rhs) <= 1e-5 * (1 + abs(rhs))     # float32 tables
+        r = oracle.rope_ref(q, c[0], s_[0])
+        assert np.allclose(r[:32] ** 2 + r[32:] ** 2, q[:32] ** 2 + q[32:] ** 2, atol=1e-5)
+
+
+def test_mla_step_absorbed_equals_explicit_with_rope():
+    """The decode step built from its pieces -- absorb the query, rotate the
+    RoPE parts, append the new token's row [c_kv | RoPE(k_pe)] to the cache,
+    absorbed attention, W_UV -- equals explicit attention on rebuilt
+    per-head keys [c_kv W_UK[h] | RoPE(k_pe)] and values c_kv W_UV[h]."""
+    rng = np.random.default_rng(41)
+    B, H, L, dc, dn, dr, dv = 2, 3, 7, 16, 8, 8, 6
+    q_nope, q_rope = rng.standard_normal((B, H, dn)), rng.standard_normal((B, H, dr))
+    c_kv, k_pe_raw = rng.standard_normal((B, L, dc)), rng.standard_normal((B, L, dr))
+    w_uk = rng.standard_normal((H, dc, dn)) / 4
+    w_uv = rng.standard_normal((H, dc, dv)) / 4
+    lens = np.array([L, 4])
+    pos_tab = rope_tables(np.arange(L), dim=dr)
+    cos, sin = (t.astype(np.float64) for t in pos_tab)
+    k_pe = oracle.rope_ref(k_pe_raw, cos[None], sin[None])      # cached keys carry their own position
+    qc = np.stack([cos[lens[b] - 1] for b in range(B)])[:, None]  # the query is the last token
+    qs = np.stack([sin[lens[b] - 1] for b in range(B)])[:, None]
+    q_rot = oracle.rope_ref(q_rope, qc, qs)
+    scale = 1 / math.sqrt(dn + dr)
+    ex, lex = oracle.mla_explicit_ref(q_nope, q_rot, c_kv, k_pe, w_uk, w_uv, lens, scale)
+    q_abs = oracle.absorb_query(q_nope, q_rot, w_uk)
+    lat, lab = oracle.mla_absorbed_ref(q_abs, np.concatenate([c_kv, k_pe], -1), lens, scale, d_v=dc)
+    out = np.stack([lat[:, h] @ w_uv[h] for h in range(H)], axis=1)
+    assert np.max(np.abs(out - ex)) <= 1e-10 and np.max(np.abs(lab - lex)) <= 1e-10
 
 
 # ---------------------------------------------------------------------------
