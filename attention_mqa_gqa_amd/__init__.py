@@ -9,7 +9,10 @@ The entry points carry the C ABI's names (see ``include/mqa_attn.h``):
   causal) and d_v != d_qk (expanded MLA prefill);
 * :func:`mqa_decode`           -- one query token per sequence vs a KV cache;
 * :func:`mla_decode_absorbed`  -- absorbed MLA decode over a latent cache;
-* :func:`mla_decode_sparse`    -- the same over selected (top-k) cache rows.
+* :func:`mla_decode_sparse`    -- the same over selected (top-k) cache rows;
+* :func:`mla_absorb_query`, :func:`mla_cache_append`,
+  :func:`mla_output_project`   -- the steps either side of the absorbed
+  decode (query absorption + RoPE, cache append + RoPE, W_UV).
 
 The library must be built (``python attention_mqa_gqa_amd/build.py``); if it
 is missing or cannot be loaded, importing the bindings raises.
@@ -35,6 +38,9 @@ __all__ = [
     "mla_decode_workspace_size",
     "mla_decode_sparse",
     "mla_decode_sparse_workspace_size",
+    "mla_absorb_query",
+    "mla_cache_append",
+    "mla_output_project",
     "DTYPE_F32",
     "DTYPE_BF16",
     "DTYPE_F16",
@@ -62,6 +68,9 @@ EXPORTED_SYMBOLS = (
     "mla_decode_absorbed",
     "mla_decode_sparse_workspace_size",
     "mla_decode_sparse",
+    "mla_absorb_query",
+    "mla_cache_append",
+    "mla_output_project",
 )
 
 
@@ -110,6 +119,12 @@ def _load():
     l.mla_decode_sparse_workspace_size.argtypes = [i, i, i]
     l.mla_decode_sparse.restype = i
     l.mla_decode_sparse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp, sz, vp]
+    l.mla_absorb_query.restype = i
+    l.mla_absorb_query.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, vp]
+    l.mla_cache_append.restype = i
+    l.mla_cache_append.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, vp]
+    l.mla_output_project.restype = i
+    l.mla_output_project.argtypes = [vp, vp, vp, i, i, i, i, vp]
     return l
 
 
@@ -330,4 +345,69 @@ def mla_decode_sparse(q_abs, kv_cache, indices, scale=None, out=None, out_dtype=
                                B, H, L_max, topk, scale, _dtype_code(q_abs.dtype), _dtype_code(out.dtype),
                                _ptr(ws), wsb, _stream_ptr(stream, q_abs.device))
     _check(st, "mla_decode_sparse")
+    return out
+
+
+def _rope_tables(cos, sin, B, torch):
+    for t, nm in ((cos, "cos"), (sin, "sin")):
+        _require(t, nm, 2)
+        if t.dtype != torch.float32 or t.shape != (B, 64):
+            raise ValueError(f"{nm} must be float32 [B, 64]")
+
+
+def mla_absorb_query(q_nope, q_rope, w_uk, cos, sin, out=None, stream=None):
+    """q_nope [B,H,128], q_rope [B,H,64], w_uk [H,512,128], cos/sin fp32 [B,64]
+    -> q_abs [B,H,576] = [W_UK[h] q_nope | RoPE(q_rope)]."""
+    torch = _torch()
+    _require(q_nope, "q_nope", 3)
+    _require(q_rope, "q_rope", 3)
+    _require(w_uk, "w_uk", 3)
+    B, H, _ = q_nope.shape
+    if q_nope.shape[2] != 128 or q_rope.shape != (B, H, 64) or w_uk.shape != (H, 512, 128):
+        raise ValueError("q_nope [B,H,128], q_rope [B,H,64], w_uk [H,512,128]")
+    _rope_tables(cos, sin, B, torch)
+    if out is None:
+        out = torch.empty((B, H, 576), dtype=q_nope.dtype, device=q_nope.device)
+    _require(out, "out", 3)
+    st = lib.mla_absorb_query(_ptr(q_nope), _ptr(q_rope), _ptr(w_uk), _ptr(cos), _ptr(sin), _ptr(out), B, H,
+                              _dtype_code(q_nope.dtype), _stream_ptr(stream, q_nope.device))
+    _check(st, "mla_absorb_query")
+    return out
+
+
+def mla_cache_append(kv_cache, c_kv, k_pe, cos, sin, positions, stream=None):
+    """kv_cache [B,L_max,576]: row positions[b] of sequence b <- [c_kv[b] | RoPE(k_pe[b])];
+    c_kv [B,512], k_pe [B,64], cos/sin fp32 [B,64], positions int32 [B]."""
+    torch = _torch()
+    _require(kv_cache, "kv_cache", 3)
+    _require(c_kv, "c_kv", 2)
+    _require(k_pe, "k_pe", 2)
+    _require(positions, "positions", 1)
+    B, L_max, _ = kv_cache.shape
+    if kv_cache.shape[2] != 576 or c_kv.shape != (B, 512) or k_pe.shape != (B, 64) or positions.shape != (B,):
+        raise ValueError("kv_cache [B,L_max,576], c_kv [B,512], k_pe [B,64], positions [B]")
+    if positions.dtype != torch.int32:
+        raise TypeError("positions must be int32")
+    _rope_tables(cos, sin, B, torch)
+    st = lib.mla_cache_append(_ptr(c_kv), _ptr(k_pe), _ptr(cos), _ptr(sin), _ptr(positions), _ptr(kv_cache), B,
+                              L_max, _dtype_code(kv_cache.dtype), _stream_ptr(stream, kv_cache.device))
+    _check(st, "mla_cache_append")
+    return kv_cache
+
+
+def mla_output_project(o_lat, w_uv, out=None, out_dtype=None, stream=None):
+    """o_lat [B,H,512], w_uv [H,512,128] -> out [B,H,128] = o_lat[b,h] W_UV[h]."""
+    torch = _torch()
+    _require(o_lat, "o_lat", 3)
+    _require(w_uv, "w_uv", 3)
+    B, H, _ = o_lat.shape
+    if o_lat.shape[2] != 512 or w_uv.shape != (H, 512, 128):
+        raise ValueError("o_lat [B,H,512], w_uv [H,512,128]")
+    out_dtype = o_lat.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((B, H, 128), dtype=out_dtype, device=o_lat.device)
+    _require(out, "out", 3)
+    st = lib.mla_output_project(_ptr(o_lat), _ptr(w_uv), _ptr(out), B, H, _dtype_code(o_lat.dtype),
+                                _dtype_code(out.dtype), _stream_ptr(stream, o_lat.device))
+    _check(st, "mla_output_project")
     return out

@@ -13,6 +13,9 @@ workload, inputs already resident in HBM:
   * mqa_prefill_ex       chunked causal MQA prefill, B=2, Hq=16, Hkv=1,
                          d=512, 1024 new tokens after 7168 (bottom-right)
   * mla_decode_sparse    batch 32, H=128, cache 32768, 2048 selected rows
+  * mla_absorb_query + mla_cache_append + mla_output_project
+                         the steps around the absorbed decode, batch 32,
+                         H=128 (weights W_UK, W_UV read once per call)
   * mqa_prefill          the first workload with fp16 inputs and output
 all bf16 in (but the last), fp32 accumulation, 16-bit out.
 
@@ -59,6 +62,7 @@ ORDER = (
     ("mla_prefill_bf16_b1_h128_t8192", "mla_prefill"),
     ("mqa_chunk_prefill_bf16_b2_q1024_kv8192", "chunk_prefill"),
     ("mla_sparse_decode_bf16_b32_l32768_k2048", "mla_sparse_decode"),
+    ("mla_step_proj_bf16_b32_h128", "mla_step_proj"),
     ("mqa_prefill_f16_b2_t4096", "f16_prefill"),
 )
 
@@ -188,7 +192,7 @@ def main():
 
     import torch
     import attention_mqa_gqa_amd as mqa
-    from synthetic import WORKLOADS, decode_inputs, draw_topk, mla_inputs, prefill_inputs
+    from synthetic import WORKLOADS, decode_inputs, draw_topk, mla_inputs, mla_step_inputs, prefill_inputs, rope_tables
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -237,6 +241,28 @@ def main():
             work[name] = dict(flops=decode_flops(s["Hq"], s["D"], sl),
                               bytes=decode_bytes(s["B"], s["Hq"], s["Hkv"], s["D"], sl), bound="hbm", shape=s,
                               mean_len=float(np.mean(sl)))
+        elif wl.kind == "mla_step":
+            B, H, L = s["B"], s["H"], s["L"]
+            qn, qr, ck, kp, wuk, wuv = (to_dev(t) for t in mla_step_inputs(B, H, seed=0))
+            pos = np.arange(B, dtype=np.int32) * 997 % L
+            cs, sn = (torch.from_numpy(t).to(dev) for t in rope_tables(pos))
+            dpos = torch.from_numpy(pos).to(dev)
+            cache = torch.zeros((B, L, 576), dtype=torch.bfloat16, device=dev)
+            q_abs = torch.empty((B, H, 576), dtype=torch.bfloat16, device=dev)
+            o_lat = to_dev(mla_inputs(B, H, 1, 512, "bf16", seed=1)[0])
+            out = torch.empty((B, H, 128), dtype=torch.bfloat16, device=dev)
+
+            def step_call(qn=qn, qr=qr, ck=ck, kp=kp, wuk=wuk, wuv=wuv, cs=cs, sn=sn, dpos=dpos, cache=cache,
+                          q_abs=q_abs, o_lat=o_lat, out=out):
+                mqa.mla_absorb_query(qn, qr, wuk, cs, sn, out=q_abs)
+                mqa.mla_cache_append(cache, ck, kp, cs, sn, dpos)
+                mqa.mla_output_project(o_lat, wuv, out=out)
+            calls[name] = step_call
+            gemm = B * H * 512 * 128
+            work[name] = dict(flops=2 * 2 * gemm,
+                              bytes=2 * (2 * H * 512 * 128 + B * H * (128 + 64 + 576 + 512 + 128) + B * (512 + 64 + 576))
+                              + 4 * B * (64 + 64 + 1),
+                              bound="hbm", shape=s)
         elif wl.kind == "mla_sparse":
             q, kv, sl = mla_inputs(s["B"], s["H"], s["L"], s["D"], "bf16", seed=0)
             idx = draw_topk(s["B"], sl, s["topk"], seed=0)

@@ -216,6 +216,46 @@ int mla_decode_sparse(const void* q_abs, const void* kv_cache, const int32_t* in
                       int dtype, int out_dtype,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------- MLA decode: the steps around it
+ * The pieces of one MLA decode step that surround mla_decode_absorbed, for
+ * the DeepSeek-V3 shapes (walkerchi.com "Full 路线" §四 4.2: latent d_c =
+ * 512, nope part 128, RoPE part d_R = 64, value 128 per head).  A step is
+ *   mla_absorb_query -> mla_cache_append -> mla_decode_absorbed
+ *   -> mla_output_project.
+ * Matrix absorption ("GQA和MLA详解" (lzwjava.github.io) §3; walkerchi §四
+ * 4.3): the per-head key up-projection folds into the query and the value
+ * up-projection is applied to the latent output.  The 64-d RoPE part is
+ * rotated by position and never absorbed ("带你了解Attention,从MHA到DeepSeek"
+ * (api.makesence.top) §4.5); the rotation is the apply_rotary_pos_emb(q, k,
+ * cos, sin) call of walkerchi §四 4.2 in rotate-half form:
+ *   RoPE(x) = x * cos + [-x[32:64] | x[0:32]] * sin,
+ * with cos, sin fp32 [B, 64] the rotary factors of each sequence's position
+ * (the caller builds them, as a model's position embeddings).
+ * dtype BF16 only (MQA_ERR_UNSUPPORTED otherwise); every pointer a device
+ * pointer, 16-byte aligned (cos / sin / positions 4-byte aligned).
+ *
+ * mla_absorb_query: q_nope [B, H, 128], q_rope [B, H, 64],
+ *   w_uk [H, 512, 128] (per head: latent x nope) ->
+ *   q_abs [B, H, 576] = [W_UK[h] q_nope (512) | RoPE(q_rope) (64)].
+ * mla_cache_append: writes the new token of each sequence,
+ *   kv_cache[b, positions[b]] = [c_kv[b] (512) | RoPE(k_pe[b]) (64)],
+ *   c_kv [B, 512], k_pe [B, 64] (before rotation), positions int32 [B] on the
+ *   device; a position outside [0, max_len) writes nothing.
+ * mla_output_project: o_lat [B, H, 512] (mla_decode_absorbed's output),
+ *   w_uv [H, 512, 128] (per head: latent x value) ->
+ *   out [B, H, 128] = o_lat[b, h] W_UV[h]; out_dtype BF16 or F32.
+ */
+int mla_absorb_query(const void* q_nope, const void* q_rope, const void* w_uk,
+                     const float* cos_t, const float* sin_t, void* q_abs,
+                     int B, int H, int dtype, void* stream);
+
+int mla_cache_append(const void* c_kv, const void* k_pe, const float* cos_t,
+                     const float* sin_t, const int32_t* positions, void* kv_cache,
+                     int B, int max_len, int dtype, void* stream);
+
+int mla_output_project(const void* o_lat, const void* w_uv, void* out,
+                       int B, int H, int dtype, int out_dtype, void* stream);
+
 #ifdef __cplusplus
 }  /* extern "C" */
 #endif

@@ -269,6 +269,10 @@ WORKLOADS = {
                  dict(B=128, Hq=64, Hkv=8, L=16384, D=128, lengths=(1024, 16384))),
         Workload("mla_decode_bf16_b32_l32768", "mla", "bf16",
                  dict(B=32, H=128, L=32768, D=576)),
+        # the steps around the absorbed MLA decode (absorption + RoPE, cache
+        # append, W_UV up-projection), batch 32, 128 heads
+        Workload("mla_step_proj_bf16_b32_h128", "mla_step", "bf16",
+                 dict(B=32, H=128, L=32768)),
         # the MQA prefill in fp16 (the zdabc.icu benchmark's GPU dtype)
         Workload("mqa_prefill_f16_b2_t4096", "prefill", "f16",
                  dict(B=2, Hq=16, Hkv=1, T=4096, D=512)),

@@ -28,7 +28,7 @@ def _declared_functions():
 
 def test_header_functions_are_exported():
     names = _declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 16, names
     assert sorted(names) == sorted(mqa.EXPORTED_SYMBOLS)
     for n in names:
         assert hasattr(lib, n), n
@@ -196,6 +196,32 @@ def test_mla_sparse_rejections():
     assert need > 0 and need % (32 * 128 * (512 + 2) * 4) == 0
     assert _sparse(wsb=need - 1) == WORKSPACE
     assert _sparse(B=0, q=None) == OK
+
+
+def test_mla_step_rejections():
+    ab = lambda **k: lib.mla_absorb_query(k.get("qn", P), k.get("qr", P), k.get("w", P), k.get("c", P),
+                                          k.get("s", P), k.get("o", P), k.get("B", 4), k.get("H", 128),
+                                          k.get("dt", BF16), None)
+    assert ab(H=0) == INVALID
+    assert ab(w=None) == INVALID
+    assert ab(c=ctypes.c_void_p(4098)) == INVALID
+    assert ab(o=MIS) == INVALID
+    assert ab(dt=F16) == UNSUPPORTED
+    assert ab(B=0, qn=None) == OK
+    ap = lambda **k: lib.mla_cache_append(k.get("c", P), k.get("k", P), P, P, k.get("pos", P), k.get("kv", P),
+                                          k.get("B", 4), k.get("L", 100), k.get("dt", BF16), None)
+    assert ap(L=0) == INVALID
+    assert ap(pos=None) == INVALID
+    assert ap(kv=MIS) == INVALID
+    assert ap(dt=F32) == UNSUPPORTED
+    assert ap(B=0, c=None) == OK
+    op = lambda **k: lib.mla_output_project(k.get("o", P), k.get("w", P), k.get("out", P), k.get("B", 4),
+                                            k.get("H", 128), k.get("dt", BF16), k.get("dout", BF16), None)
+    assert op(H=-1) == INVALID
+    assert op(out=None) == INVALID
+    assert op(dt=BF16, dout=F16) == UNSUPPORTED
+    assert op(dt=F32, dout=F32) == UNSUPPORTED
+    assert op(B=0, o=None) == OK
 
 
 def test_decode_workspace_grows_with_splits():

@@ -15,8 +15,8 @@ import numpy as np
 import pytest
 
 import oracle
-from synthetic import (decode_inputs, decode_slice, mla_inputs, mla_slice, prefill_inputs,
-                       round_bf16, draw_lengths, draw_topk)
+from synthetic import (decode_inputs, decode_slice, mla_inputs, mla_slice, mla_step_inputs, prefill_inputs,
+                       rope_tables, round_bf16, draw_lengths, draw_topk)
 
 pytestmark = pytest.mark.gpu
 
@@ -404,6 +404,94 @@ def test_decode_f16(torch, mqa, B, Hq, Hkv, L, D, lengths, odt):
     _say(f"  max |err| {err:.2e}")
     assert err <= F16_TOL
     assert _maxerr(host(lse), ref_lse) <= F16_TOL
+
+
+# ---------------------------------------------------------------------------
+# the steps around absorbed MLA decode: absorption + RoPE, cache append,
+# output up-projection, and one whole decode step
+# ---------------------------------------------------------------------------
+
+def _cs(torch, positions):
+    c, s_ = rope_tables(positions)
+    return (torch.from_numpy(c).cuda(), torch.from_numpy(s_).cuda(), c.astype(np.float64), s_.astype(np.float64))
+
+
+def test_mla_absorb_query(torch, mqa):
+    _say("mla absorb query B37 H128")
+    B, H = 37, 128
+    qn, qr, _, _, wuk, _ = mla_step_inputs(B, H, seed=20)
+    pos = np.random.default_rng(20).integers(0, 40000, size=B)
+    dc, ds, c, s_ = _cs(torch, pos)
+    q_abs = mqa.mla_absorb_query(dev(torch, qn), dev(torch, qr), dev(torch, wuk), dc, ds)
+    torch.cuda.synchronize()
+    ref = oracle.absorb_query(qn.f32(), oracle.rope_ref(qr.f32(), c[:, None], s_[:, None]), wuk.f32())
+    assert _maxerr(host(q_abs), ref) <= BF16_TOL
+
+
+def test_mla_cache_append(torch, mqa):
+    _say("mla cache append B5 L64")
+    B, L = 5, 64
+    _, _, ckv, kpe, _, _ = mla_step_inputs(B, 16, seed=21)
+    pos = np.array([0, 63, 17, 64, -1], dtype=np.int32)          # the last two are outside the cache: skipped
+    dc, ds, c, s_ = _cs(torch, np.clip(pos, 0, None))
+    cache = torch.zeros((B, L, 576), dtype=torch.bfloat16, device="cuda")
+    mqa.mla_cache_append(cache, dev(torch, ckv), dev(torch, kpe), dc, ds, torch.from_numpy(pos).cuda())
+    torch.cuda.synchronize()
+    got = host(cache)
+    rot = oracle.rope_ref(kpe.f32(), c, s_)
+    for b in range(B):
+        if 0 <= pos[b] < L:
+            row = got[b, pos[b]]
+            assert np.array_equal(row[:512], ckv.f32()[b])                      # copied bits
+            assert np.max(np.abs(row[512:] - rot[b])) <= 2 ** -8 * max(1.0, np.max(np.abs(rot[b])))
+            got[b, pos[b]] = 0
+    assert not got.any()                                                        # nothing else written
+
+
+@pytest.mark.parametrize("B,odt", [(40, "bf16"), (16, "f32"), (3, "bf16")])
+def test_mla_output_project(torch, mqa, B, odt):
+    _say(f"mla output projection B{B} H128 out={odt}")
+    H = 128
+    _, _, _, _, _, wuv = mla_step_inputs(1, H, seed=22)
+    o_lat, _, _ = mla_inputs(B, H, 1, 512, "bf16", seed=22)                   # any bf16 [B, H, 512]
+    out_dtype = torch.float32 if odt == "f32" else torch.bfloat16
+    out = mqa.mla_output_project(dev(torch, o_lat), dev(torch, wuv), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ref = np.einsum("bhc,hcv->bhv", o_lat.f32().astype(np.float64), wuv.f32().astype(np.float64))
+    assert _maxerr(host(out), ref) <= (F32_TOL * 100 if odt == "f32" else BF16_TOL)
+
+
+def test_mla_decode_step_end_to_end(torch, mqa):
+    """Cache built token by token with mla_cache_append, then one step:
+    mla_absorb_query -> mla_decode_absorbed -> mla_output_project, against
+    explicit attention on rebuilt per-head keys [c_kv W_UK | RoPE(k_pe)] and
+    values c_kv W_UV (bf16 intermediates: q_abs, cache, o_lat)."""
+    _say("mla decode step end to end B4 H128 L48")
+    B, H, L = 4, 128, 48
+    qn, qr, _, _, wuk, wuv = mla_step_inputs(B, H, seed=23)
+    lens = np.array([48, 1, 30, 17], dtype=np.int32)
+    rng = np.random.default_rng(23)
+    from synthetic import Tensor, bf16_bits
+    ckv_all = Tensor(bf16_bits(rng.standard_normal((B, L, 512), dtype=np.float32)), "bf16")
+    kpe_all = Tensor(bf16_bits(rng.standard_normal((B, L, 64), dtype=np.float32)), "bf16")
+    cache = torch.zeros((B, L, 576), dtype=torch.bfloat16, device="cuda")
+    dck, dkp = dev(torch, ckv_all), dev(torch, kpe_all)
+    for t in range(L):
+        pos = np.where(t < lens, t, -1).astype(np.int32)
+        dc, ds, _, _ = _cs(torch, np.full(B, t))
+        mqa.mla_cache_append(cache, dck[:, t].contiguous(), dkp[:, t].contiguous(), dc, ds,
+                             torch.from_numpy(pos).cuda())
+    dc, ds, c, s_ = _cs(torch, lens - 1)
+    q_abs = mqa.mla_absorb_query(dev(torch, qn), dev(torch, qr), dev(torch, wuk), dc, ds)
+    o_lat = mqa.mla_decode_absorbed(q_abs, cache, torch.from_numpy(lens).cuda())
+    out = mqa.mla_output_project(o_lat, dev(torch, wuv), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    tc, ts = (t.astype(np.float64) for t in rope_tables(np.arange(L)))
+    k_rot = oracle.rope_ref(kpe_all.f32(), tc[None], ts[None])
+    q_rot = oracle.rope_ref(qr.f32(), c[:, None], s_[:, None])
+    ref, _ = oracle.mla_explicit_ref(qn.f32(), q_rot, ckv_all.f32(), k_rot, wuk.f32(), wuv.f32(), lens,
+                                     1 / math.sqrt(192))
+    assert _maxerr(host(out), ref) <= BF16_TOL
 
 
 # ---------------------------------------------------------------------------
