@@ -70,8 +70,16 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
     char* const pbuf = smem + kNS * kStageB;                    // [2][kPB]
     float* const alpha_buf = (float*)(pbuf + 2 * kPB);          // [2][kHMAX]
 
-    const int s_idx = blockIdx.x;
-    const int b = blockIdx.y;
+    // Workgroups are dealt to the XCDs round-robin by flat index; when the
+    // batch splits evenly over the XCDs, all splits of one sequence go to
+    // one XCD, so its q_abs rows are fetched once into that XCD's L2.
+    int s_idx = blockIdx.x, b = blockIdx.y;
+    if (gridDim.y % kNumXcd == 0) {
+        const int f = (int)(blockIdx.x + gridDim.x * blockIdx.y);
+        const int x = f % kNumXcd, slot = f / kNumXcd;
+        b = (slot / (int)gridDim.x) * kNumXcd + x;
+        s_idx = slot % (int)gridDim.x;
+    }
     // positions begin .. end-1 of the row list (cache rows, or list entries)
     const int L = SPARSE ? topk : min(max(seq_lens[b], 0), max_len);
     const int begin = s_idx * chunk;
