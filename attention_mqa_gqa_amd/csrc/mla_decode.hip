@@ -188,139 +188,221 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
         for (int nt = 0; nt < NT; ++nt) o[mt][nt] = f32x16{};
     float m_run = -INFINITY, l_run = 0.f;
 
-    // Tile t lives in stage t % 3.  Iteration t: scores and softmax of t,
-    // P(t) and the per-head rescale factors to LDS, barrier, then copies of
-    // tile t+2 (into the stage of tile t-1, whose P.V every wave finished
-    // before the barrier) and P(t).V(t).  Tiles t+1 and t+2 are in flight
-    // meanwhile; each wave waits for its own copies of t+1 before the barrier.
-    issue(0);
-    if (n_tiles > 1) issue(1);
-    if (n_tiles > 1) wait_vmcnt<kCopiesPerWave>(); else wait_vmcnt<0>();
-    __syncthreads();
-
-    for (int it = 0; it < n_tiles; ++it) {
-        const char* st = smem + (it % kNS) * kStageB;
-
-        // ---- S^T = KV q_abs^T ------------------------------------------------
-        f32x16 s = f32x16{};
-        {
-            bf16x8 abuf[PF];
+    // ---- scores of one tile: S^T = KV q_abs^T (heads 32w + n, keys
+    // 8(i/4) + 4h2 + i%4) ------------------------------------------------------
+    auto scores = [&](const char* st) {
+        f32x16 sc = f32x16{};
+        bf16x8 abuf[PF];
 #pragma unroll
-            for (int j = 0; j < PF; ++j) abuf[j] = kread(st, j);
+        for (int j = 0; j < PF; ++j) abuf[j] = kread(st, j);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 a = abuf[ks % PF];
-                if (ks + PF < KS) abuf[ks % PF] = kread(st, ks + PF);
-                s = mfma_32x32x16(a, qb[ks], s);
-            }
-            sched_reads_ahead<PF, KS - PF>();
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 a = abuf[ks % PF];
+            if (ks + PF < KS) abuf[ks % PF] = kread(st, ks + PF);
+            sc = mfma_32x32x16(a, qb[ks], sc);
         }
+        sched_reads_ahead<PF, KS - PF>();
+        return sc;
+    };
 
-        // ---- online softmax of heads 32w + n (keys 8(i/4) + 4h2 + i%4) ---------
-        // the scale is > 0, so the row max is taken on the raw scores and
-        // the scale folds into the exponent: p = 2^(s * c - m)
-        const int row0 = begin + it * kKT;
-        float mloc = -INFINITY;
+    // ---- online softmax, in three pieces so that it can sit between MFMAs --
+    // (1) mask, row max, lazy rescale: returns the exponent reference.  The
+    // scale is > 0, so the row max is taken on the raw scores and the scale
+    // folds into the exponent: p = 2^(s * c - m).  A tile past the chunk end
+    // is all masked: it changes nothing and writes P = 0.
+    float alpha_t = 1.f;
+    auto sm_max = [&](f32x16& sc, int tile) {
+        const int row0 = begin + tile * kKT;
         if constexpr (SPARSE) {
             // one validity bit per list entry of the tile (lane n: entry n)
             const bool ok = row0 + n < end && sidx[min(row0 + n, end - 1) - begin] >= 0;
             const uint32_t vm = (uint32_t)__ballot(ok);
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-                if (!((vm >> (8 * (i >> 2) + 4 * h2 + (i & 3))) & 1u)) s[i] = -INFINITY;
+                if (!((vm >> (8 * (i >> 2) + 4 * h2 + (i & 3))) & 1u)) sc[i] = -INFINITY;
         } else if (row0 + kKT > end) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int key = row0 + 8 * (i >> 2) + 4 * h2 + (i & 3);
-                if (key >= end) s[i] = -INFINITY;
+                if (key >= end) sc[i] = -INFINITY;
             }
         }
+        float mloc = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) mloc = max3f(mloc, s[2 * i], s[2 * i + 1]);
+        for (int i = 0; i < 8; ++i) mloc = max3f(mloc, sc[2 * i], sc[2 * i + 1]);
         const float mx = max_over_halves(mloc) * scale_log2;
-        float alpha = 1.f;
+        alpha_t = 1.f;
         if (mx > m_run + kRescaleSlack) {
             const float mnew = fmaxf(m_run, mx);
-            alpha = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - mnew);
+            alpha_t = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - mnew);
             m_run = mnew;
-            l_run *= alpha;
+            l_run *= alpha_t;
         }
-        // a sparse chunk can start with tiles of skipped entries only: then
-        // m_run is still -inf and every p must be 0 (2^(-inf - 0))
+    };
+    // (2) exponentials of accumulators 4c .. 4c+3, packed, to P(tile) in LDS.
+    // A sparse chunk can start with tiles of skipped entries only: then
+    // m_run is still -inf and every p must be 0 (2^(-inf - 0)).
+    auto sm_exp = [&](f32x16& sc, int tile, int c) {
         const float m_use = (SPARSE && m_run == -INFINITY) ? 0.f : m_run;
-        float lsum = 0.f;
+        float p[4];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            s[i] = fast_exp2(fmaf(s[i], scale_log2, -m_use));
-            lsum += s[i];
+        for (int i = 0; i < 4; ++i) {
+            p[i] = fast_exp2(fmaf(sc[4 * c + i], scale_log2, -m_use));
+            l_run += p[i];
         }
-        l_run += lsum;
-        {
-            char* pl = pbuf + (it & 1) * kPB + head * 64 + 8 * h2;
-            const int sw = layout::ptile_swz(head);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                u32x2 pk;
-                pk.x = pack_bf16x2(s[4 * c + 0], s[4 * c + 1]);
-                pk.y = pack_bf16x2(s[4 * c + 2], s[4 * c + 3]);
-                *(u32x2*)(pl + ((c ^ sw) * 16)) = pk;
-            }
-            if (h2 == 0) alpha_buf[(it & 1) * kHMAX + head] = alpha;
-        }
+        u32x2 pk;
+        pk.x = pack_bf16x2(p[0], p[1]);
+        pk.y = pack_bf16x2(p[2], p[3]);
+        char* pl = pbuf + (tile & 1) * kPB + head * 64 + 8 * h2;
+        *(u32x2*)(pl + ((c ^ layout::ptile_swz(head)) * 16)) = pk;
+    };
+    // (3) the per-head rescale factor of the tile
+    auto sm_alpha = [&](int tile) {
+        if (h2 == 0) alpha_buf[(tile & 1) * kHMAX + head] = alpha_t;
+    };
 
-        // tile it+1 has landed (nothing later was issued yet)
+    // ---- O^T += V^T P^T for value dims 128w .. 128w+127, all heads ------------
+    // 8 steps (kp, mt), each one V^T operand x 4 P^T operands; between(stp)
+    // runs after step stp's MFMAs (work placed between them).  The MFMAs are
+    // opaque to the scheduler, so the software pipeline is pinned with
+    // scheduling fences: V^T reads run two steps ahead and the P^T operands
+    // of kp = 1 are read during kp = 0.
+    auto pv_tile = [&](int it, auto&& between) {
+        const char* st = smem + (it % kNS) * kStageB;
+        const char* pl = pbuf + (it & 1) * kPB;
+        auto pread = [&](int kp, int nt) {
+            const int hh = 32 * nt + n;
+            return *(const bf16x8*)(pl + hh * 64 + (((2 * kp + h2) ^ layout::ptile_swz(hh)) * 16));
+        };
+        constexpr int NSTEP = 2 * MT;
+        bf16x8 pb[2][NT];
+        bf16x8 va[3];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) pb[0][nt] = pread(0, nt);
+        va[0] = vread(st, 0, 0);
+        va[1] = vread(st, 0, 1);
+        const float* al = alpha_buf + (it & 1) * kHMAX;
+        float a4[NT];
+        bool need = false;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            a4[nt] = al[32 * nt + n];
+            need |= a4[nt] != 1.f;
+        }
+        between(-1);
+        if (__any(need)) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) scale_acc(o[mt][nt], a4[nt]);
+        }
+#pragma unroll
+        for (int stp = 0; stp < NSTEP; ++stp) {
+            if (stp + 2 < NSTEP) va[(stp + 2) % 3] = vread(st, (stp + 2) / MT, (stp + 2) % MT);
+            if (stp == 1) {
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) pb[1][nt] = pread(1, nt);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) mfma_32x32x16_acc(va[stp % 3], pb[stp / MT][nt], o[stp % MT][nt]);
+            between(stp);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // Tile t lives in stage t % 3.
+    issue(0);
+    if (n_tiles > 1) issue(1);
+    if (n_tiles > 1) wait_vmcnt<kCopiesPerWave>(); else wait_vmcnt<0>();
+    __syncthreads();
+    if constexpr (!SPARSE) {
+        // Iteration t (entered with tile t+1 landed and P(t) in LDS): copies
+        // of tile t+2 (into the stage of tile t-1, whose P.V every wave
+        // finished before the barrier), the scores of tile t+1, then
+        // P(t).V(t) with the softmax of tile t+1 and the writes of P(t+1)
+        // between its MFMAs, and a barrier once tile t+2 has landed.  On the
+        // last iteration the scores of the (absent) next tile read a stale
+        // stage and are masked away.
+        {
+            f32x16 s0 = scores(smem);
+            sm_max(s0, 0);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) sm_exp(s0, 0, c);
+            sm_alpha(0);
+        }
         wait_vmcnt<0>();
         __syncthreads();
-        const bool copy_next = it + 2 < n_tiles;
-
-        // ---- O^T += V^T P^T for value dims 128w .. 128w+127, all heads ------------
-        // 8 steps (kp, mt), each one V^T operand x 4 P^T operands.  The
-        // MFMAs are opaque to the scheduler, so the software pipeline is
-        // pinned with scheduling fences: V^T reads run two steps ahead and
-        // the P^T operands of kp = 1 are read during kp = 0.
-        {
-            const char* pl = pbuf + (it & 1) * kPB;
-            auto pread = [&](int kp, int nt) {
-                const int hh = 32 * nt + n;
-                return *(const bf16x8*)(pl + hh * 64 + (((2 * kp + h2) ^ layout::ptile_swz(hh)) * 16));
-            };
-            constexpr int NSTEP = 2 * MT;
-            bf16x8 pb[2][NT];
-            bf16x8 va[3];
+        for (int it = 0; it < n_tiles; ++it) {
+            if (it + 2 < n_tiles) issue(it + 2);
+            f32x16 sn = scores(smem + ((it + 1) % kNS) * kStageB);
+            // P(t).V(t) as in pv_tile (written out: the register allocator
+            // fits this loop without spills only in this form), with the
+            // softmax of the next tile: max after step 1, exponentials and P
+            // writes over steps 2..5, the rescale factor at 6
+            {
+                const char* st = smem + (it % kNS) * kStageB;
+                const char* pl = pbuf + (it & 1) * kPB;
+                auto pread = [&](int kp, int nt) {
+                    const int hh = 32 * nt + n;
+                    return *(const bf16x8*)(pl + hh * 64 + (((2 * kp + h2) ^ layout::ptile_swz(hh)) * 16));
+                };
+                constexpr int NSTEP = 2 * MT;
+                bf16x8 pb[2][NT];
+                bf16x8 va[3];
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) pb[0][nt] = pread(0, nt);
-            va[0] = vread(st, 0, 0);
-            va[1] = vread(st, 0, 1);
-            const float* al = alpha_buf + (it & 1) * kHMAX;
-            float a4[NT];
-            bool need = false;
+                for (int nt = 0; nt < NT; ++nt) pb[0][nt] = pread(0, nt);
+                va[0] = vread(st, 0, 0);
+                va[1] = vread(st, 0, 1);
+                const float* al = alpha_buf + (it & 1) * kHMAX;
+                float a4[NT];
+                bool need = false;
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                a4[nt] = al[32 * nt + n];
-                need |= a4[nt] != 1.f;
-            }
-            // The copies of tile it+2 go out while the reads above are in
-            // flight: the memory pipeline takes one 1 KB copy at a time, so
-            // the issuing wave waits here either way.
-            if (copy_next) issue(it + 2);
-            if (__any(need)) {
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) scale_acc(o[mt][nt], a4[nt]);
-            }
-#pragma unroll
-            for (int stp = 0; stp < NSTEP; ++stp) {
-                if (stp + 2 < NSTEP) va[(stp + 2) % 3] = vread(st, (stp + 2) / MT, (stp + 2) % MT);
-                if (stp == 1) {
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) pb[1][nt] = pread(1, nt);
+                for (int nt = 0; nt < NT; ++nt) {
+                    a4[nt] = al[32 * nt + n];
+                    need |= a4[nt] != 1.f;
                 }
-                __builtin_amdgcn_sched_barrier(0);
+                if (__any(need)) {
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) mfma_32x32x16_acc(va[stp % 3], pb[stp / MT][nt], o[stp % MT][nt]);
-                __builtin_amdgcn_sched_barrier(0);
+                    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt) scale_acc(o[mt][nt], a4[nt]);
+                }
+#pragma unroll
+                for (int stp = 0; stp < NSTEP; ++stp) {
+                    if (stp + 2 < NSTEP) va[(stp + 2) % 3] = vread(st, (stp + 2) / MT, (stp + 2) % MT);
+                    if (stp == 1) {
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt) pb[1][nt] = pread(1, nt);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) mfma_32x32x16_acc(va[stp % 3], pb[stp / MT][nt], o[stp % MT][nt]);
+                    if (stp == 1) sm_max(sn, it + 1);
+                    if (stp >= 2 && stp < 6) sm_exp(sn, it + 1, stp - 2);
+                    if (stp == 6) sm_alpha(it + 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
+            wait_vmcnt<0>();
+            __syncthreads();
+        }
+    } else {
+        // Sparse chunks are short (a few tiles), so they keep two tiles in
+        // flight instead: iteration t computes the scores and softmax of t,
+        // barrier, then copies of tile t+2 and P(t).V(t).
+        for (int it = 0; it < n_tiles; ++it) {
+            f32x16 sc = scores(smem + (it % kNS) * kStageB);
+            sm_max(sc, it);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) sm_exp(sc, it, c);
+            sm_alpha(it);
+            // tile it+1 has landed (nothing later was issued yet)
+            wait_vmcnt<0>();
+            __syncthreads();
+            pv_tile(it, [&](int stp) {
+                if (stp == -1 && it + 2 < n_tiles) issue(it + 2);
+            });
         }
     }
 
