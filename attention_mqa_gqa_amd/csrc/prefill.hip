@@ -214,12 +214,10 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     const int n_tiles = CAUSAL ? ((t_last + q_off) / KT + 1) : n_kv_tiles;
 
     // LDS: K stages 0/1, then V^T stages 0/1; tile j lives in stage j & 1.
-    // Iteration t computes S(t+1) next to softmax(t) (between barriers A and
-    // B), then P(t).V(t).  Right after barrier A it copies V(t+1) into the
-    // stage of V(t-1) (read by P(t-1).V(t-1), before A); right after barrier
-    // B it copies K(t+3) into the stage of K(t+1) (read by S(t+1), before B).
-    // Copies are issued in the order they are consumed, so in-order vmcnt
-    // waits are exact.
+    // Iteration t starts with one barrier (K(t+1) and V(t) have landed; every
+    // wave is done with S(t), which read K(t), and with P(t-1).V(t-1)), copies
+    // K(t+2) into the stage of K(t) and V(t+1) into the stage of V(t-1), then
+    // computes S(t+1) next to softmax(t), then P(t).V(t).
     const uint32_t lds_base = lds_addr(smem);
     const uint32_t lane16 = (uint32_t)lane * 16u;
     auto issue_k = [&](int tile) {
@@ -334,8 +332,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     };
     const float c = scale_log2;
 
-    // prologue: copies K(0), K(1), V(0); S(0); then K(2) once every wave is
-    // done with K(0).  Global copy order: K0 K1 V0 K2 | V1 K3 | V2 K4 | ...
+    // prologue: copies K(0), K(1), V(0); S(0).
     issue_k(0);
     if (n_tiles > 1) issue_k(1);
     issue_v(0);
@@ -345,8 +342,6 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
 #pragma unroll
     for (int nt = 0; nt < NR; ++nt) sA[nt] = f32x16{};
     s_all(sA, smem);
-    __syncthreads();
-    if (n_tiles > 2) issue_k(2);
     if (tile_masked(0)) mask_tile(sA, 0);
 #pragma unroll
     for (int nt = 0; nt < NR; ++nt) {
@@ -357,29 +352,28 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     }
 
     // Iteration t (scores of tile t in sc, masked, row max folded into m_run):
+    //   barrier, copies of K(t+2) and V(t+1);
     //   phase A: S(t+1) MFMAs, with the exponentials, row sums and bf16
     //            packing of P(t) placed between them;
     //   phase B: P(t).V(t) MFMAs, with the masking and row max of S(t+1)
     //            between them; then the (rare) lazy rescale for tile t+1.
     // Each phase is a fixed sequence of chunks separated by scheduling
-    // fences, so MFMA latency is filled with this wave's VALU work.  Right
-    // after barrier A, V(t+1) is copied into the stage of V(t-1); right
-    // after barrier B, K(t+3) into the stage of K(t+1).  Copies are issued
-    // in the order they are consumed, so in-order vmcnt waits are exact.
+    // fences, so MFMA latency is filled with this wave's VALU work.  The
+    // copies issued at iteration t are the only ones in flight and must
+    // land before iteration t+1, so the wait is for all of them.
     // The score buffers alternate between sA and sB (loop unrolled by 2).
     constexpr int NSTEP_PV = KSP * MT_O;
     auto body = [&](int it, f32x16 (&sc)[NR], f32x16 (&sn)[NR]) {
         const bool has_next = it + 1 < n_tiles;
-        const bool has_next2 = it + 2 < n_tiles;
-        // K(it+1) has landed; V(it) and K(it+2) may still be in flight
-        if (has_next) wait_vmcnt_of<LHK, LHV>(LHV + (has_next2 ? LHK : 0));
+        // K(it+1) and V(it) have landed
+        wait_vmcnt<0>();
         __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();                                       // barrier A
+        __syncthreads();
 
         // ---- phase A: S(it+1) (unconditionally: on the last tile it reads a
         // stale but valid K stage and is discarded) | exp of S(it) ----------
-        // The first K operand reads go out before the V(it+1) copies, whose
-        // issue then covers their latency.
+        // The first K operand reads go out before the copies, whose issue
+        // then covers their latency.
         const char* kst = smem + ((it + 1) & 1) * KSTAGE_B;
 #pragma unroll
         for (int nt = 0; nt < NR; ++nt) sn[nt] = f32x16{};
@@ -390,6 +384,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
             bf16x8 abuf[PF];
 #pragma unroll
             for (int j = 0; j < PF; ++j) abuf[j] = kread(kst, j);
+            if (it + 2 < n_tiles) issue_k(it + 2);
             if (has_next) issue_v(it + 1);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
@@ -420,19 +415,13 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
                 f32x4 hi = {sc[nt][8 * kp + 4], sc[nt][8 * kp + 5], sc[nt][8 * kp + 6], sc[nt][8 * kp + 7]};
                 pb[nt][kp] = pack8_t<F16>(lo, hi);
                 // keeps the exponentials in phase A: without a use here the
-                // compiler sinks them past barrier B to the P.V MFMAs
+                // compiler sinks them into phase B, next to the P.V MFMAs
                 asm volatile("" : "+v"(pb[nt][kp]));
             }
         }
 
-        // V(it) has landed (K(it+2) and V(it+1) may still be in flight)
-        wait_vmcnt_of<LHK, LHV>((has_next2 ? LHK : 0) + (has_next ? LHV : 0));
-        __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();                                       // barrier B
-
         // ---- phase B: O^T += V^T P^T (contraction step outer, head-dim tile
         // inner, V^T reads PF steps ahead) | row max of S(it+1) --------------
-        // As in phase A, the first operand reads precede the copies.
         float mloc[NR];
 #pragma unroll
         for (int nt = 0; nt < NR; ++nt) mloc[nt] = -INFINITY;
@@ -446,7 +435,6 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
             };
 #pragma unroll
             for (int st = 0; st < PF; ++st) vbuf[st] = *(const bf16x8*)vaddr(st);
-            if (it + 3 < n_tiles) issue_k(it + 3);
             if (has_next && tile_masked(it + 1)) mask_tile(sn, it + 1);
 #pragma unroll
             for (int st = 0; st < NSTEP_PV; ++st) {
