@@ -215,9 +215,13 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
 
     // LDS: K stages 0/1, then V^T stages 0/1; tile j lives in stage j & 1.
     // Iteration t starts with one barrier (K(t+1) and V(t) have landed; every
-    // wave is done with S(t), which read K(t), and with P(t-1).V(t-1)), copies
-    // K(t+2) into the stage of K(t) and V(t+1) into the stage of V(t-1), then
-    // computes S(t+1) next to softmax(t), then P(t).V(t).
+    // wave is done with S(t), which read K(t), and with P(t-1).V(t-1)), then
+    // computes S(t+1) next to softmax(t) while copying K(t+2) into the stage
+    // of K(t), then P(t).V(t); V(t+1) goes into the stage of V(t-1) at the
+    // start of one of the two phases.  With one wave per SIMD (d_qk = 512)
+    // the copies are split over both phases (measured 3.7 % faster); with two
+    // waves per SIMD both go in phase A (6 % faster at d_qk = 192).
+    constexpr bool V_IN_B = KPAD;
     const uint32_t lds_base = lds_addr(smem);
     const uint32_t lane16 = (uint32_t)lane * 16u;
     auto issue_k = [&](int tile) {
@@ -352,11 +356,13 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     }
 
     // Iteration t (scores of tile t in sc, masked, row max folded into m_run):
-    //   barrier, copies of K(t+2) and V(t+1);
-    //   phase A: S(t+1) MFMAs, with the exponentials, row sums and bf16
-    //            packing of P(t) placed between them;
-    //   phase B: P(t).V(t) MFMAs, with the masking and row max of S(t+1)
-    //            between them; then the (rare) lazy rescale for tile t+1.
+    //   barrier;
+    //   phase A: copies of K(t+2) (and V(t+1)); S(t+1) MFMAs, with the
+    //            exponentials, row sums and bf16 packing of P(t) placed
+    //            between them;
+    //   phase B: (copies of V(t+1)); P(t).V(t) MFMAs, with the masking and
+    //            row max of S(t+1) between them; then the (rare) lazy
+    //            rescale for tile t+1.
     // Each phase is a fixed sequence of chunks separated by scheduling
     // fences, so MFMA latency is filled with this wave's VALU work.  The
     // copies issued at iteration t are the only ones in flight and must
@@ -385,7 +391,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
 #pragma unroll
             for (int j = 0; j < PF; ++j) abuf[j] = kread(kst, j);
             if (it + 2 < n_tiles) issue_k(it + 2);
-            if (has_next) issue_v(it + 1);
+            if (!V_IN_B && has_next) issue_v(it + 1);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const bf16x8 a = abuf[ks % PF];
@@ -435,6 +441,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
             };
 #pragma unroll
             for (int st = 0; st < PF; ++st) vbuf[st] = *(const bf16x8*)vaddr(st);
+            if (V_IN_B && has_next) issue_v(it + 1);
             if (has_next && tile_masked(it + 1)) mask_tile(sn, it + 1);
 #pragma unroll
             for (int st = 0; st < NSTEP_PV; ++st) {
