@@ -222,19 +222,23 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     // the copies are split over both phases (measured 3.7 % faster); with two
     // waves per SIMD both go in phase A (6 % faster at d_qk = 192).
     constexpr bool V_IN_B = KPAD;
+    static_assert(!V_IN_B || LHV % 4 == 0, "V copies in phase B go by groups of four");
     const uint32_t lds_base = lds_addr(smem);
     const uint32_t lane16 = (uint32_t)lane * 16u;
+    // copy group g (of FK / 4) of a padded K tile: four padded 1 KB rows,
+    // identical in the stream and in LDS, four copies per M0 write
+    auto issue_k_group = [&](int tile, int g) {
+        const char* src = KVbh + (size_t)tile * TILE_B;
+        const uint32_t dst = lds_base + (uint32_t)((tile & 1) * KSTAGE_B);
+        const int row = (g * NW + w) * 4;
+        if constexpr (KPAD) copy4_to_lds_async<KROW_B>(src + row * KROW_B, lane16, dst + (uint32_t)(row * KROW_B));
+    };
     auto issue_k = [&](int tile) {
         const char* src = KVbh + (size_t)tile * TILE_B;
         const uint32_t dst = lds_base + (uint32_t)((tile & 1) * KSTAGE_B);
         if constexpr (KPAD) {
-            // padded 1 KB rows, identical in the stream and in LDS: runs of
-            // four rows, four copies per M0 write
 #pragma unroll
-            for (int g = 0; g < FK / 4; ++g) {
-                const int row = (g * NW + w) * 4;
-                copy4_to_lds_async<KROW_B>(src + row * KROW_B, lane16, dst + (uint32_t)(row * KROW_B));
-            }
+            for (int g = 0; g < FK / 4; ++g) issue_k_group(tile, g);
         } else {
 #pragma unroll
             for (int i = 0; i < FK; ++i) {
@@ -249,17 +253,20 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
             if (lane < PLK) copy16_to_lds_async(src + off, lane16, dst + off);
         }
     };
+    // copy group g (of LHV / 4) of a V^T tile: V^T tiles are contiguous in
+    // both places, so each wave copies runs of 4 KB, four copies per M0 write
+    auto issue_v_group = [&](int tile, int g) {
+        const char* src = KVbh + (size_t)tile * TILE_B + KSTAGE_B;
+        const uint32_t dst = lds_base + (uint32_t)(2 * KSTAGE_B + (tile & 1) * VSTAGE_B);
+        const int inst = (g * NW + w) * 4;
+        copy4x1k_to_lds_async(src + inst * 1024, lane16, dst + (uint32_t)inst * 1024u);
+    };
     auto issue_v = [&](int tile) {
         const char* src = KVbh + (size_t)tile * TILE_B + KSTAGE_B;
         const uint32_t dst = lds_base + (uint32_t)(2 * KSTAGE_B + (tile & 1) * VSTAGE_B);
         if constexpr (LHV % 4 == 0) {
-            // V^T tiles are contiguous in both places: each wave copies runs of
-            // 4 KB, four copies per M0 write
 #pragma unroll
-            for (int g = 0; g < LHV / 4; ++g) {
-                const int inst = (g * NW + w) * 4;
-                copy4x1k_to_lds_async(src + inst * 1024, lane16, dst + (uint32_t)inst * 1024u);
-            }
+            for (int g = 0; g < LHV / 4; ++g) issue_v_group(tile, g);
         } else {
 #pragma unroll
             for (int i = 0; i < LHV; ++i) {
@@ -390,10 +397,14 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
             bf16x8 abuf[PF];
 #pragma unroll
             for (int j = 0; j < PF; ++j) abuf[j] = kread(kst, j);
-            if (it + 2 < n_tiles) issue_k(it + 2);
+            if (!KPAD && it + 2 < n_tiles) issue_k(it + 2);
             if (!V_IN_B && has_next) issue_v(it + 1);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
+                // padded K: the copy groups spread evenly over the phase
+                if constexpr (KPAD) {
+                    if (ks % (KS / (FK / 4)) == 0 && it + 2 < n_tiles) issue_k_group(it + 2, ks / (KS / (FK / 4)));
+                }
                 const bf16x8 a = abuf[ks % PF];
                 if (ks + PF < KS) abuf[ks % PF] = kread(kst, ks + PF);
 #pragma unroll
@@ -441,10 +452,13 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
             };
 #pragma unroll
             for (int st = 0; st < PF; ++st) vbuf[st] = *(const bf16x8*)vaddr(st);
-            if (V_IN_B && has_next) issue_v(it + 1);
             if (has_next && tile_masked(it + 1)) mask_tile(sn, it + 1);
 #pragma unroll
             for (int st = 0; st < NSTEP_PV; ++st) {
+                // V(t+1) in this phase: the copy groups spread evenly over it
+                if constexpr (V_IN_B) {
+                    if (st % (NSTEP_PV / (LHV / 4)) == 0 && has_next) issue_v_group(it + 1, st / (NSTEP_PV / (LHV / 4)));
+                }
                 const bf16x8 a = vbuf[st % PF];
                 if (st + PF < NSTEP_PV) vbuf[st % PF] = *(const bf16x8*)vaddr(st + PF);
                 const int kp = st / MT_O, mt = st % MT_O;
