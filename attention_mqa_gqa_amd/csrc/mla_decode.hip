@@ -190,13 +190,15 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
 
     // ---- scores of one tile: S^T = KV q_abs^T (heads 32w + n, keys
     // 8(i/4) + 4h2 + i%4) ------------------------------------------------------
-    auto scores = [&](const char* st) {
+    // between(ks) runs before step ks's MFMA (work spread over the phase)
+    auto scores = [&](const char* st, auto&& between) {
         f32x16 sc = f32x16{};
         bf16x8 abuf[PF];
 #pragma unroll
         for (int j = 0; j < PF; ++j) abuf[j] = kread(st, j);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
+            between(ks);
             const bf16x8 a = abuf[ks % PF];
             if (ks + PF < KS) abuf[ks % PF] = kread(st, ks + PF);
             sc = mfma_32x32x16(a, qb[ks], sc);
@@ -204,6 +206,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
         sched_reads_ahead<PF, KS - PF>();
         return sc;
     };
+    auto nothing = [](int) {};
 
     // ---- online softmax, in three pieces so that it can sit between MFMAs --
     // (1) mask, row max, lazy rescale: returns the exponent reference.  The
@@ -325,7 +328,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
         // last iteration the scores of the (absent) next tile read a stale
         // stage and are masked away.
         {
-            f32x16 s0 = scores(smem);
+            f32x16 s0 = scores(smem, nothing);
             sm_max(s0, 0);
 #pragma unroll
             for (int c = 0; c < 4; ++c) sm_exp(s0, 0, c);
@@ -334,8 +337,12 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
         wait_vmcnt<0>();
         __syncthreads();
         for (int it = 0; it < n_tiles; ++it) {
-            if (it + 2 < n_tiles) issue(it + 2);
-            f32x16 sn = scores(smem + ((it + 1) % kNS) * kStageB);
+            // copies of tile t+2 spread over the score MFMAs, one every
+            // four steps
+            const bool copy_next = it + 2 < n_tiles;
+            f32x16 sn = scores(smem + ((it + 1) % kNS) * kStageB, [&](int ks) {
+                if (ks % 4 == 0 && ks / 4 < kCopiesPerWave && copy_next) issue_one(it + 2, ks / 4);
+            });
             // P(t).V(t) as in pv_tile (written out: the register allocator
             // fits this loop without spills only in this form), with the
             // softmax of the next tile: max after step 1, exponentials and P
@@ -392,7 +399,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
         // flight instead: iteration t computes the scores and softmax of t,
         // barrier, then copies of tile t+2 and P(t).V(t).
         for (int it = 0; it < n_tiles; ++it) {
-            f32x16 sc = scores(smem + (it % kNS) * kStageB);
+            f32x16 sc = scores(smem + (it % kNS) * kStageB, nothing);
             sm_max(sc, it);
 #pragma unroll
             for (int c = 0; c < 4; ++c) sm_exp(sc, it, c);
