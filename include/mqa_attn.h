@@ -89,8 +89,8 @@ const char* mqa_last_hip_error_name(void);
  *   scale: the factor on Q.K^T, normally 1/sqrt(D).  Must be finite and > 0.
  * Supported: Hq % Hkv == 0;
  *   in_dtype BF16 or F16 -> out_dtype the same or F32, D in {128, 512}, and the group
- *     size G = Hq/Hkv a power of two with G <= 128 (D=512) or G <= 256
- *     (D=128);
+ *     size G = Hq/Hkv <= 128 (D=512) or G <= 256 (D=128) (any G: a
+ *     workgroup takes floor(rows / G) tokens of all G heads);
  *   in_dtype F32 -> out_dtype F32, D a multiple of 64 up to 512, any G.
  * Workspace: 16-bit inputs need `mqa_prefill_workspace_size()` bytes, where the
  * library first writes K and a transposed V as one stream of 32-key tiles

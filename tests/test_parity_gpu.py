@@ -88,6 +88,8 @@ PREFILL_SMALL = [
     (1, 32, 1, 40, 128, True, "bf16"),
     (1, 128, 1, 20, 512, True, "f32"),
     (1, 12, 4, 65, 128, False, "bf16"),
+    (1, 12, 1, 99, 512, True, "bf16"),        # group of 12 (not a power of two): 10 tokens per block
+    (2, 6, 1, 70, 128, True, "f32"),          # group of 6
 ]
 
 
@@ -259,6 +261,31 @@ def test_prefill_ex_full_size_sampled(torch, mqa, B, Hq, Hkv, Tq, Tkv, DK, DV):
     assert bool(torch.isfinite(out.float()).all())
 
 
+def test_calls_follow_the_given_stream(torch, mqa):
+    """The library enqueues on the stream it is given: work queued on a side
+    stream behind a long kernel still reads the inputs as they are when it
+    runs, and the result is the same as on the default stream."""
+    _say("prefill + decode on a side stream")
+    q, k, v = prefill_inputs(1, 16, 1, 300, 512, "bf16", seed=12)
+    dq, dk, dv = dev(torch, q), dev(torch, k), dev(torch, v)
+    ref = mqa.mqa_prefill(dq, dk, dv, causal=True)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        out = mqa.mqa_prefill(dq, dk, dv, causal=True, stream=side)
+    side.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    qd, kc, vc, sl = decode_inputs(3, 16, 1, 500, 512, "bf16", seed=12, lengths=[500, 7, 260])
+    dsl = torch.from_numpy(sl).cuda()
+    a = mqa.mqa_decode(dev(torch, qd), dev(torch, kc), dev(torch, vc), dsl)
+    with torch.cuda.stream(side):
+        b = mqa.mqa_decode(dev(torch, qd), dev(torch, kc), dev(torch, vc), dsl, stream=side)
+    side.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
 # ---------------------------------------------------------------------------
 # decode
 # ---------------------------------------------------------------------------
@@ -270,6 +297,7 @@ DECODE_SMALL = [
     (3, 8, 8, 700, 128, [700, 3, 64], "bf16"),
     (2, 12, 3, 300, 512, [299, 300], "f32"),
     (3, 16, 16, 100, 128, [1, 2, 100], "bf16"),
+    (2, 12, 1, 900, 512, [900, 333], "bf16"),  # group of 12 (padded to 16 MFMA columns)
 ]
 
 
