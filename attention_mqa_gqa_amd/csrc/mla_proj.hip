@@ -50,6 +50,9 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const bf16* __restrict_
                                                          const float* __restrict__ sinv, bf16* __restrict__ q_abs,
                                                          int B, int H) {
     constexpr int KS = kDn / 16;     // 8 contraction steps
+    // the 32 sequences x 128 latent dims of one sweep step, staged so that
+    // each sequence's 256 bytes leave in 16-byte stores
+    __shared__ __attribute__((aligned(16))) bf16 stage[32][128 + 8];
     const int h = blockIdx.x;
     const int lane = lane_id();
     const int w = wave_id();
@@ -74,26 +77,32 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const bf16* __restrict_
             acc = mfma_32x32x16(wa[ks], __builtin_bit_cast(bf16x8, ok ? v : u32x4{0, 0, 0, 0}), acc);
         }
         // accumulator i: latent row c0 + 8(i/4) + 4 h2 + i%4, sequence b
-        if (ok) {
-            bf16* dst = q_abs + ((size_t)b * H + h) * kDq + c0 + 4 * h2;
+        __syncthreads();                         // the previous step's stores have read the stage
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                u32x2 pk;
-                pk.x = pack_bf16x2(acc[4 * q + 0], acc[4 * q + 1]);
-                pk.y = pack_bf16x2(acc[4 * q + 2], acc[4 * q + 3]);
-                *(u32x2*)(dst + 8 * q) = pk;
-            }
+        for (int q = 0; q < 4; ++q) {
+            u32x2 pk;
+            pk.x = pack_bf16x2(acc[4 * q + 0], acc[4 * q + 1]);
+            pk.y = pack_bf16x2(acc[4 * q + 2], acc[4 * q + 3]);
+            *(u32x2*)&stage[n][32 * w + 8 * q + 4 * h2] = pk;
+        }
+        __syncthreads();
+        // 32 rows x 16 chunks of 16 bytes, 256 threads: two chunks each
+        for (int e = (int)threadIdx.x; e < 32 * 16; e += 256) {
+            const int r = e >> 4, ch = e & 15;
+            if (b0 + r < B)
+                *(u32x4*)(q_abs + ((size_t)(b0 + r) * H + h) * kDq + blockIdx.y * 128 + 8 * ch) =
+                    *(const u32x4*)&stage[r][8 * ch];
         }
     }
 
-    // RoPE part of q_abs (latent block 0 of each head does it)
-    if (blockIdx.y == 0) {
-        for (int e = (int)threadIdx.x; e < B * kDr; e += 256) {
-            const int b = e / kDr, d = e % kDr;
-            const float y = rope_elem(q_rope + ((size_t)b * H + h) * kDr, d, cosv + (size_t)b * kDr,
-                                      sinv + (size_t)b * kDr);
-            q_abs[((size_t)b * H + h) * kDq + kDc + d] = (bf16)y;
-        }
+    // RoPE part of q_abs: latent block y rotates dims 16 y .. 16 y + 15
+    constexpr int kRd = kDr / (kDc / 128);
+#pragma unroll 2
+    for (int e = (int)threadIdx.x; e < B * kRd; e += 256) {
+        const int b = e / kRd, d = kRd * blockIdx.y + e % kRd;
+        const float y = rope_elem(q_rope + ((size_t)b * H + h) * kDr, d, cosv + (size_t)b * kDr,
+                                  sinv + (size_t)b * kDr);
+        q_abs[((size_t)b * H + h) * kDq + kDc + d] = (bf16)y;
     }
 }
 
@@ -135,22 +144,28 @@ __global__ __launch_bounds__(256) void mla_out_proj_kernel(const bf16* __restric
     for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     const bf16* wh = w_uv + (size_t)h * kDc * kDv;
     const bf16* orow = o_lat + ((size_t)(ok ? b : 0) * H + h) * kDc;
-#pragma unroll 2
+    // every load of the wave is issued before the first product: 32 KB of
+    // W_UV[h] per wave in flight at once
+    u32x4 r[NSTEP][4];
+    u32x2 bop[NSTEP];
+#pragma unroll
     for (int st = 0; st < NSTEP; ++st) {
         const int c = 128 * w + 16 * st + 4 * g;     // latent dims c .. c+3 of this lane group
-        u32x4 r[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) r[j] = ldg16(wh + (size_t)(c + j) * kDv + 8 * m);   // W_UV[h][c+j][8m..8m+7]
-        const u32x2 bop = ok ? *(const u32x2*)(orow + c) : u32x2{0, 0};
+        for (int j = 0; j < 4; ++j) r[st][j] = ldg16(wh + (size_t)(c + j) * kDv + 8 * m);   // W_UV[h][c+j][8m..8m+7]
+        bop[st] = ok ? *(const u32x2*)(orow + c) : u32x2{0, 0};
+    }
+#pragma unroll
+    for (int st = 0; st < NSTEP; ++st) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             // A operand of M-tile t: row m <-> value dim 8m + t, slot j <-> latent dim c + j
             const uint32_t sel = (t & 1) ? kSelHiHalves : kSelLoHalves;
             const int wd = t >> 1;
             u32x2 a;
-            a.x = perm(r[1][wd], r[0][wd], sel);
-            a.y = perm(r[3][wd], r[2][wd], sel);
-            acc[t] = mfma_16x16x16(a, bop, acc[t]);
+            a.x = perm(r[st][1][wd], r[st][0][wd], sel);
+            a.y = perm(r[st][3][wd], r[st][2][wd], sel);
+            acc[t] = mfma_16x16x16(a, bop[st], acc[t]);
         }
     }
     // acc[t][i]: value dim 8(4g + i) + t, sequence b0 + m

@@ -38,6 +38,7 @@ from .attention_ref import (  # noqa: F401
     mla_absorbed_ref,
     mla_explicit_ref,
     mla_sparse_ref,
+    output_project,
     partial_ref,
     prefill_ref,
     prefill_rows_ref,

@@ -37,6 +37,7 @@ __all__ = [
     "mla_sparse_ref",
     "rope_ref",
     "absorb_query",
+    "output_project",
     "mla_explicit_ref",
     "kv_values_per_token",
 ]
@@ -294,6 +295,20 @@ def absorb_query(q_nope, q_rope, w_uk):
     for h in range(H):
         lat[:, h] = q_nope[:, h] @ w_uk[h].T
     return np.concatenate([lat, q_rope], axis=-1)
+
+
+def output_project(o_lat, w_uv):
+    """Map the absorbed decode's latent output back to value space (lzwjava
+    §3; walkerchi §四 4.3): with V_h = c_kv @ W_UV[h], softmax . V_h =
+    (softmax . c_kv) @ W_UV[h], so head h's output is o_lat[:, h] @ W_UV[h].
+    o_lat [B, H, d_c]; w_uv [H, d_c, d_v].  Returns [B, H, d_v].
+    """
+    o_lat, w_uv = _f64(o_lat), _f64(w_uv)
+    B, H, _ = o_lat.shape
+    out = np.empty((B, H, w_uv.shape[2]))
+    for h in range(H):
+        out[:, h] = o_lat[:, h] @ w_uv[h]
+    return out
 
 
 def mla_explicit_ref(q_nope, q_rope, c_kv, k_pe, w_uk, w_uv, seq_lens, scale):

@@ -436,10 +436,20 @@ def test_o7_absorbed_equals_explicit():
     q_abs = oracle.absorb_query(q_nope, q_rope, w_uk)
     latent = np.concatenate([c_kv, k_pe], axis=-1)
     o_lat, l_abs = oracle.mla_absorbed_ref(q_abs, latent, lens, scale, d_v=c_kv.shape[-1])
-    H = q_nope.shape[1]
-    out = np.stack([o_lat[:, h] @ w_uv[h] for h in range(H)], axis=1)   # caller's W_UV step
+    out = oracle.output_project(o_lat, w_uv)
     assert np.max(np.abs(out - explicit)) <= 1e-10
     assert np.max(np.abs(l_abs - l_exp)) <= 1e-10
+
+
+def test_o7_output_project_brute_force():
+    """Pure-Python sums: out[b, h, v] = sum_c o_lat[b, h, c] W_UV[h][c, v]."""
+    rng = np.random.default_rng(34)
+    o_lat, w_uv = rng.standard_normal((2, 3, 5)), rng.standard_normal((3, 5, 4))
+    out = oracle.output_project(o_lat, w_uv)
+    for b in range(2):
+        for h in range(3):
+            for v in range(4):
+                assert abs(out[b, h, v] - sum(o_lat[b, h, c] * w_uv[h, c, v] for c in range(5))) <= 1e-12
 
 
 def test_o7_absorbed_query_closed_form():
@@ -531,7 +541,7 @@ def test_mla_step_absorbed_equals_explicit_with_rope():
     ex, lex = oracle.mla_explicit_ref(q_nope, q_rot, c_kv, k_pe, w_uk, w_uv, lens, scale)
     q_abs = oracle.absorb_query(q_nope, q_rot, w_uk)
     lat, lab = oracle.mla_absorbed_ref(q_abs, np.concatenate([c_kv, k_pe], -1), lens, scale, d_v=dc)
-    out = np.stack([lat[:, h] @ w_uv[h] for h in range(H)], axis=1)
+    out = oracle.output_project(lat, w_uv)
     assert np.max(np.abs(out - ex)) <= 1e-10 and np.max(np.abs(lab - lex)) <= 1e-10
 
 

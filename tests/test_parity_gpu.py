@@ -485,7 +485,7 @@ def test_mla_output_project(torch, mqa, B, odt):
     out_dtype = torch.float32 if odt == "f32" else torch.bfloat16
     out = mqa.mla_output_project(dev(torch, o_lat), dev(torch, wuv), out_dtype=out_dtype)
     torch.cuda.synchronize()
-    ref = np.einsum("bhc,hcv->bhv", o_lat.f32().astype(np.float64), wuv.f32().astype(np.float64))
+    ref = oracle.output_project(o_lat.f32(), wuv.f32())
     assert _maxerr(host(out), ref) <= (F32_TOL * 100 if odt == "f32" else BF16_TOL)
 
 
