@@ -413,7 +413,11 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
                 for (int i = ks * 16 / KS; i < (ks + 1) * 16 / KS; ++i) {
 #pragma unroll
                     for (int nt = 0; nt < NR; ++nt) {
-                        const float pr = fast_exp2(fmaf(sc[nt][i], c, -m_run[nt]));
+                        // pinned to this step: otherwise the exponentials
+                        // are sunk past the copy-group branch and bunch up
+                        // between two MFMAs
+                        float pr = fast_exp2(fmaf(sc[nt][i], c, -m_run[nt]));
+                        asm volatile("" : "+v"(pr));
                         sc[nt][i] = pr;
                         lsum[nt] += pr;
                     }
