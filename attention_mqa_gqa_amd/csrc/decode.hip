@@ -26,11 +26,46 @@
 
 namespace mqa {
 
+// Sequences are taken longest first: workgroup z works on the sequence whose
+// rank by (clamped length descending, index ascending) is z.  With ragged
+// lengths the workgroups of the longest sequences then start in the first
+// round of resident workgroups instead of forming the tail.  Batches above
+// kSortMax keep the identity order, and so does a grid that is resident
+// all at once (sort = false: the order cannot matter there).  Returns the
+// sequence; its clamped length goes to *len.
+constexpr int kSortMax = 256;
+template <int NT>
+__device__ __forceinline__ int longest_first(const int32_t* __restrict__ seq_lens, int B, int max_len, int z,
+                                             bool sort, int* sl, int* pick, int* len) {
+    static_assert(NT >= kSortMax, "one thread per sequence");
+    if (!sort || B <= 1 || B > kSortMax) {
+        *len = min(max(seq_lens[z], 0), max_len);
+        return z;
+    }
+    const int t = (int)threadIdx.x;
+    if (t < B) sl[t] = min(max(seq_lens[t], 0), max_len);
+    __syncthreads();
+    if (t < B) {
+        const int lt = sl[t];
+        int r = 0;
+#pragma unroll 8
+        for (int u = 0; u < B; ++u) {
+            const int lu = sl[u];
+            r += (lu > lt) | ((lu == lt) & (u < t));
+        }
+        if (r == z) *pick = t;
+    }
+    __syncthreads();
+    const int b = *pick;
+    *len = sl[b];
+    return b;
+}
+
 template <int D, int KSUB, int NW, bool F16>
 __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(
     const bf16* __restrict__ Qp, const bf16* __restrict__ Kc, const bf16* __restrict__ Vc,
     const int32_t* __restrict__ seq_lens, float* __restrict__ part_o, float* __restrict__ part_ml, int Hq,
-    int Hkv, int max_len, int G, int chunk, int n_split, float scale_log2) {
+    int Hkv, int max_len, int G, int chunk, int n_split, float scale_log2, int sort) {
     constexpr int KS = D / 32;     // QK^T contraction steps (16x16x32)
     constexpr int NSL = D / 128;   // V slices of 128 head dims
     constexpr int MT_O = D / 16;   // O^T M-tiles
@@ -41,10 +76,14 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(
     __shared__ float sm_l[NW][16];
     __shared__ __attribute__((aligned(16))) float sm_o[NW][16][PAD];
 
+    __shared__ int sm_len[kSortMax];
+    __shared__ int sm_pick;
+
     const int s_idx = blockIdx.x;
     const int hk = blockIdx.y;
-    const int b = blockIdx.z;
-    const int L = min(max(seq_lens[b], 0), max_len);
+    int L;
+    const int b = longest_first<NW * 64>(seq_lens, (int)gridDim.z, max_len, (int)blockIdx.z, sort != 0, sm_len,
+                                         &sm_pick, &L);
     const int wg_begin = s_idx * chunk;
     if (wg_begin >= L) return;                       // whole workgroup: uniform exit
     const int wg_end = min(wg_begin + chunk, L);
@@ -53,7 +92,10 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_split_kernel(
     const int w = wave_id();
     const int g = lane >> 4;
     const int n = lane & 15;
-    const int per_wave = chunk / NW;
+    // the rows this workgroup really has (fewer than chunk at the end of a
+    // sequence) split evenly over its waves, 16-row aligned; a wave whose
+    // share starts past wg_end idles
+    const int per_wave = ((wg_end - wg_begin + NW - 1) / NW + 15) / 16 * 16;
     const int k_begin = wg_begin + w * per_wave;
     const int k_end = min(k_begin + per_wave, wg_end);
 
@@ -297,13 +339,30 @@ DecodePlan decode_plan(int B, int Hkv, int max_len, int head_dim) {
     return p;
 }
 
+// Workgroups of one decode kernel that the device holds at once (queried
+// once per kernel); 0 if the query fails.
+template <int D, int KSUB, bool F16>
+static long resident_wgs() {
+    static const long n = [] {
+        int dev = 0, cus = 0, per_cu = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<D, KSUB, 4, F16>, 256, 0) !=
+                hipSuccess)
+            return 0L;
+        return (long)cus * per_cu;
+    }();
+    return n;
+}
+
 hipError_t decode_launch(const DecodeArgs& a) {
     const float sl2 = a.scale * kLog2e;
     const dim3 grid(a.plan.n_split, a.Hkv, a.B);
+    const long wgs = (long)a.plan.n_split * a.Hkv * a.B;
 #define MQA_DECODE(D, KSUB, F16)                                                                              \
     hipLaunchKernelGGL((decode_split_kernel<D, KSUB, 4, F16>), grid, dim3(256), 0, a.stream, (const bf16*)a.q,    \
                        (const bf16*)a.k, (const bf16*)a.v, a.seq_lens, a.part_o, a.part_ml, a.Hq, a.Hkv, a.max_len, \
-                       a.G, a.plan.chunk, a.plan.n_split, sl2)
+                       a.G, a.plan.chunk, a.plan.n_split, sl2, (int)(wgs > resident_wgs<D, KSUB, F16>()))
     if (a.D == 512) {
         if (a.f16) MQA_DECODE(512, 1, true); else MQA_DECODE(512, 1, false);
     } else if (a.D == 128) {

@@ -298,6 +298,10 @@ DECODE_SMALL = [
     (2, 12, 3, 300, 512, [299, 300], "f32"),
     (3, 16, 16, 100, 128, [1, 2, 100], "bf16"),
     (2, 12, 1, 900, 512, [900, 333], "bf16"),  # group of 12 (padded to 16 MFMA columns)
+    # more workgroups than the device holds at once: sequences taken longest
+    # first (B <= 256), and in index order above that
+    (160, 16, 8, 600, 128, (1, 600), "bf16"),
+    (300, 8, 8, 64, 128, (1, 64), "f32"),
 ]
 
 
