@@ -526,6 +526,56 @@ def test_mla_decode_step_end_to_end(torch, mqa):
     assert _maxerr(host(out), ref) <= BF16_TOL
 
 
+def test_mla_step_graph_replay(torch, mqa):
+    """A whole absorbed decode step (absorb + RoPE, cache append, absorbed
+    attention with its merge, W_UV) captured once in a HIP graph through the
+    C ABI and replayed: every replay, with the program's own eager work and
+    synchronisations in between, equals the eager step bit for bit."""
+    _say("mla decode step as a HIP graph B6 H128 L96")
+    B, H, L = 6, 128, 96
+    qn, qr, ckv, kpe, wuk, wuv = (dev(torch, t) for t in mla_step_inputs(B, H, seed=24))
+    lens = np.array([96, 1, 50, 95, 17, 64], dtype=np.int32)
+    pos = torch.from_numpy(lens - 1).cuda()
+    dsl = torch.from_numpy(lens).cuda()
+    dc, ds, _, _ = _cs(torch, lens - 1)
+    rng = np.random.default_rng(24)
+    from synthetic import Tensor, bf16_bits
+    cache0 = dev(torch, Tensor(bf16_bits(rng.standard_normal((B, L, 576), dtype=np.float32)), "bf16"))
+    q_abs = torch.empty((B, H, 576), dtype=torch.bfloat16, device="cuda")
+    o_lat = torch.empty((B, H, 512), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((B, H, 128), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(mqa.mla_decode_workspace_size(B, H, L), dtype=torch.uint8, device="cuda")
+    cache = cache0.clone()
+
+    def step():
+        mqa.mla_absorb_query(qn, qr, wuk, dc, ds, out=q_abs)
+        mqa.mla_cache_append(cache, ckv, kpe, dc, ds, pos)
+        mqa.mla_decode_absorbed(q_abs, cache, dsl, out=o_lat, workspace=ws)
+        mqa.mla_output_project(o_lat, wuv, out=out)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (q_abs, cache, o_lat, out)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()                                   # warm-up on the capture stream's side
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        for t in (q_abs, o_lat, out):
+            t.zero_()                            # eager work between replays
+        cache.copy_(cache0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((q_abs, cache, o_lat, out), ref):
+            assert torch.equal(got, want), f"replay {rep}"
+
+
 # ---------------------------------------------------------------------------
 # sparse (top-k) MLA decode
 # ---------------------------------------------------------------------------
