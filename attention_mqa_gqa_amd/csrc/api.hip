@@ -70,8 +70,10 @@ size_t mqa_prefill_ex_workspace_size(int B, int Hq, int Hkv, int T_q, int T_kv, 
     const mqa::PrefillPlan p = mqa::prefill_plan(d_qk, d_v, 1);
     if (p.kt <= 0) return 0;
     const size_t tiles = ((size_t)T_kv + p.kt - 1) / p.kt;
-    // K tile (padded rows at d_qk = 512) + V^T tile, 16-bit elements
-    return (size_t)B * Hkv * tiles * ((size_t)mqa::layout::prefill_k_tile_bytes(p.kt, d_qk) + (size_t)p.kt * d_v * 2);
+    // V^T tile, 16-bit elements, and at d_qk = 512 the padded K tile
+    // (narrower K rows are copied from K itself)
+    const size_t k_tile = d_qk == 512 ? (size_t)mqa::layout::prefill_k_tile_bytes(p.kt, d_qk) : 0;
+    return (size_t)B * Hkv * tiles * (k_tile + (size_t)p.kt * d_v * 2);
 }
 
 size_t mqa_prefill_workspace_size(int B, int Hq, int Hkv, int T, int head_dim, int in_dtype) {

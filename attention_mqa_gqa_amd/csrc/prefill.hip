@@ -31,16 +31,17 @@ namespace mqa {
 
 // ---------------------------------------------------------------------------
 // K [B*Hkv, T, DK], V [B*Hkv, T, DV] -> tile stream
-// [B*Hkv, n_tiles, (K tile | V^T tile)].
+// [B*Hkv, n_tiles, (K tile | V^T tile)] for DK = 512, [B*Hkv, n_tiles,
+// V^T tile] otherwise.
 // Each 32-key tile is stored exactly as the prefill kernel keeps it in LDS:
-// the K tile row-major (row = key; 16-byte chunks in swizzled order, except
-// rows of exactly 1 KB, which are stored in plain order with 16 bytes of
-// padding, key layout::padded_row_pos(p) at row position p) and the V^T tile
-// (row = value dim, 32 keys per row, swizzled chunks), zero past T.  V's
-// contraction index (the key) is its row index, so the P.V operand needs it
-// transposed; doing that here once, and storing both tiles contiguously,
-// turns every global->LDS copy of the main kernel into a straight 16-byte
-// stream (uniform base + 16 * lane).
+// the V^T tile (row = value dim, 32 keys per row, swizzled chunks), zero
+// past T, and for 1 KB rows the K tile (row-major, plain chunk order with 16
+// bytes of padding per row, key layout::padded_row_pos(p) at row position
+// p).  V's contraction index (the key) is its row index, so the P.V operand
+// needs it transposed; doing that here once turns every V copy of the main
+// kernel into a straight 16-byte stream (uniform base + 16 * lane).  Narrower
+// K rows need no packing: the main kernel copies them from K itself, the
+// chunk swizzle folded into its per-lane source offsets.
 // ---------------------------------------------------------------------------
 template <int DK, int DV, int KT>
 __global__ __launch_bounds__(256) void kv_pack_kernel(const bf16* __restrict__ K, const bf16* __restrict__ V,
@@ -49,8 +50,8 @@ __global__ __launch_bounds__(256) void kv_pack_kernel(const bf16* __restrict__ K
     constexpr int ROW_CHUNKS = DK / 8;   // 16-byte chunks per K row
     constexpr int NB = RL * (DV / 8);    // 8x8 blocks per V tile
     constexpr bool KPAD = (2 * DK == 1024);
-    constexpr int KTILE_B = layout::prefill_k_tile_bytes(KT, DK);
-    constexpr int KROW_B = KTILE_B / KT;
+    constexpr int KTILE_B = KPAD ? layout::prefill_k_tile_bytes(KT, DK) : 0;   // packed K bytes per tile
+    constexpr int KROW_B = layout::prefill_k_tile_bytes(KT, DK) / KT;
     constexpr int TILE_V = KT * DV;
     const int tile = blockIdx.x;
     const size_t bh = blockIdx.y;
@@ -60,7 +61,7 @@ __global__ __launch_bounds__(256) void kv_pack_kernel(const bf16* __restrict__ K
     bf16* vdst = (bf16*)(kdst + KTILE_B);
     // K tile: chunk position p of row position kk holds global chunk
     // p ^ swz(kk) of key kk, or (1 KB rows) chunk p of key padded_row_pos(kk)
-    for (int q = threadIdx.x; q < KT * ROW_CHUNKS; q += 256) {
+    for (int q = threadIdx.x; KPAD && q < KT * ROW_CHUNKS; q += 256) {
         const int kk = q / ROW_CHUNKS;
         const int p = q % ROW_CHUNKS;
         const int c = KPAD ? p : (p ^ layout::swz32(kk, ROW_CHUNKS));
@@ -110,7 +111,7 @@ __global__ __launch_bounds__(256) void kv_pack_kernel(const bf16* __restrict__ K
 // ---------------------------------------------------------------------------
 template <int DK, int DV, int NR, int NW, int KT, bool CAUSAL, bool OUT_F32, bool F16>
 __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
-    const bf16* __restrict__ Q, const bf16* __restrict__ KVt,
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ KVt,
     void* __restrict__ Out, float* __restrict__ Lse, int Hq, int Hkv, int Tq, int Tkv, int q_off,
     int G, int tok_per_wg, int n_tok_blocks, int n_kv_tiles, int xcd_map, float scale_log2) {
     constexpr int RW = 32 * NR;           // rows per wave
@@ -207,8 +208,11 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
     }
 
     const size_t bh = (size_t)b * Hkv + hk;
-    constexpr int TILE_B = KSTAGE_B + 2 * TILE_V;      // bytes per tile in the stream
+    // tile stream: (padded K tile |) V^T tile; narrower K rows come from K
+    constexpr int KSTREAM_B = KPAD ? KSTAGE_B : 0;
+    constexpr int TILE_B = KSTREAM_B + 2 * TILE_V;     // bytes per tile in the stream
     const char* KVbh = (const char*)KVt + bh * (size_t)n_kv_tiles * TILE_B;
+    const uint64_t Kg = (uint64_t)(uintptr_t)(K + bh * (size_t)Tkv * DK);
 
     const int t_last = min(Tq, t0 + tok_per_wg) - 1;
     const int n_tiles = CAUSAL ? ((t_last + q_off) / KT + 1) : n_kv_tiles;
@@ -233,36 +237,51 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_bf16_kernel(
         const int row = (g * NW + w) * 4;
         if constexpr (KPAD) copy4_to_lds_async<KROW_B>(src + row * KROW_B, lane16, dst + (uint32_t)(row * KROW_B));
     };
+    // Unpadded K tiles are copied from K itself: LDS byte o of a tile is
+    // chunk (o % row) / 16 of row r = o / row, which holds chunk
+    // c ^ swz32(r) of key r; k_src gives that chunk's byte offset from the
+    // tile's first key row (rows at or past the tile's row_lim valid rows
+    // read the last valid one, masked later).
+    auto k_src = [&](int o, int row_lim) -> uint32_t {
+        const int r = o / (2 * DK), c = (o % (2 * DK)) / 16;
+        return (uint32_t)(min(r, row_lim - 1) * (2 * DK) + ((c ^ layout::swz32(r, ROW_CHUNKS)) * 16));
+    };
+    auto k_copy_byte = [&](int i) {      // LDS byte of this lane in K copy i
+        return i < FK ? (i * NW + w) * 1024 + lane * 16 : FK * NW * 1024 + w * PLK * 16 + lane * 16;
+    };
     auto issue_k = [&](int tile) {
-        const char* src = KVbh + (size_t)tile * TILE_B;
         const uint32_t dst = lds_base + (uint32_t)((tile & 1) * KSTAGE_B);
         if constexpr (KPAD) {
 #pragma unroll
             for (int g = 0; g < FK / 4; ++g) issue_k_group(tile, g);
         } else {
+            const void* src = (const void*)(uintptr_t)(Kg + (uint64_t)tile * (KT * 2 * DK));
+            const int row_lim = min(Tkv - tile * KT, KT);    // valid rows of this tile (wave-uniform)
 #pragma unroll
             for (int i = 0; i < FK; ++i) {
                 const int inst = i * NW + w;               // wave-uniform
-                copy16_to_lds_async(src + inst * 1024, lane16, dst + (uint32_t)inst * 1024u);
+                const uint32_t off = k_src(k_copy_byte(i), row_lim);
+                copy16_to_lds_async(src, off, dst + (uint32_t)inst * 1024u);
             }
-        }
-        if constexpr (PLK != 0) {
-            // last round: wave w copies bytes [FK NW 1 KB + 16 PLK w, +16 PLK)
-            // of the (unpadded) tile with its first PLK lanes
-            const uint32_t off = (uint32_t)(FK * NW * 1024 + w * PLK * 16);
-            if (lane < PLK) copy16_to_lds_async(src + off, lane16, dst + off);
+            if constexpr (PLK != 0) {
+                // last round: wave w copies bytes [FK NW 1 KB + 16 PLK w, +16 PLK)
+                // of the tile with its first PLK lanes
+                const uint32_t lds_off = (uint32_t)(FK * NW * 1024 + w * PLK * 16);
+                const uint32_t off = k_src(min(k_copy_byte(FK), TILE_K * 2 - 16), row_lim);
+                if (lane < PLK) copy16_to_lds_async(src, off, dst + lds_off);
+            }
         }
     };
     // copy group g (of LHV / 4) of a V^T tile: V^T tiles are contiguous in
     // both places, so each wave copies runs of 4 KB, four copies per M0 write
     auto issue_v_group = [&](int tile, int g) {
-        const char* src = KVbh + (size_t)tile * TILE_B + KSTAGE_B;
+        const char* src = KVbh + (size_t)tile * TILE_B + KSTREAM_B;
         const uint32_t dst = lds_base + (uint32_t)(2 * KSTAGE_B + (tile & 1) * VSTAGE_B);
         const int inst = (g * NW + w) * 4;
         copy4x1k_to_lds_async(src + inst * 1024, lane16, dst + (uint32_t)inst * 1024u);
     };
     auto issue_v = [&](int tile) {
-        const char* src = KVbh + (size_t)tile * TILE_B + KSTAGE_B;
+        const char* src = KVbh + (size_t)tile * TILE_B + KSTREAM_B;
         const uint32_t dst = lds_base + (uint32_t)(2 * KSTAGE_B + (tile & 1) * VSTAGE_B);
         if constexpr (LHV % 4 == 0) {
 #pragma unroll
@@ -634,7 +653,7 @@ static hipError_t launch_16(const PrefillArgs& a) {
     const int xcd_map = P % kNumXcd == 0 ? 1 : (kNumXcd % P == 0 && n_tok_blocks % (kNumXcd / P) == 0 ? 2 : 0);
 #define MQA_PREFILL_LAUNCH(C, F)                                                                              \
     hipLaunchKernelGGL((prefill_bf16_kernel<DK, DV, NR, NW, KT, C, F, F16>), grid, dim3(NW * 64), 0, a.stream, \
-                       (const bf16*)a.q, (const bf16*)kvt, a.out, a.lse, a.Hq, a.Hkv, a.Tq, a.Tkv, q_off, a.G, \
+                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)kvt, a.out, a.lse, a.Hq, a.Hkv, a.Tq, a.Tkv, q_off, a.G, \
                        tok, n_tok_blocks, n_kv_tiles, xcd_map, sl2)
     if (a.causal) {
         if (a.out_f32) MQA_PREFILL_LAUNCH(true, true); else MQA_PREFILL_LAUNCH(true, false);

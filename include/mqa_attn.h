@@ -93,10 +93,10 @@ const char* mqa_last_hip_error_name(void);
  *     workgroup takes floor(rows / G) tokens of all G heads);
  *   in_dtype F32 -> out_dtype F32, D a multiple of 64 up to 512, any G.
  * Workspace: 16-bit inputs need `mqa_prefill_workspace_size()` bytes, where the
- * library first writes K and a transposed V as one stream of 32-key tiles
- * (B * Hkv * ceil(T/32) * 32 * (2 D + pad) * 2 bytes, pad = 8 elements per
- * key when D = 512, else 0); F32 needs none (workspace may be NULL with
- * workspace_bytes 0).
+ * library first writes a transposed V, and at D = 512 also K with padded
+ * rows, as one stream of 32-key tiles (B * Hkv * ceil(T/32) * 32 * (D + k)
+ * * 2 bytes, k = D + 8 when D = 512, else 0: narrower K rows are read from K
+ * itself); F32 needs none (workspace may be NULL with workspace_bytes 0).
  */
 size_t mqa_prefill_workspace_size(int B, int Hq, int Hkv, int T, int head_dim,
                                   int in_dtype);
@@ -131,8 +131,8 @@ int mqa_prefill(const void* q, const void* k, const void* v, void* out, float* l
  *   plus (d_qk, d_v) = (192, 128) with any G <= 256 (16-bit) or any G (fp32).
  *   T_q == 0 or B == 0 is an empty call; T_kv == 0 with T_q > 0 is rejected.
  * Workspace (16-bit inputs): `mqa_prefill_ex_workspace_size()` bytes =
- *   B * Hkv * ceil(T_kv/32) * 32 * (d_qk + pad + d_v) * 2, pad = 8 when
- *   d_qk = 512 (16 bytes per 1 KB key row), else 0; F32 needs none.
+ *   B * Hkv * ceil(T_kv/32) * 32 * (k + d_v) * 2, k = d_qk + 8 when
+ *   d_qk = 512 (padded 1 KB key rows), else 0; F32 needs none.
  * mqa_prefill(..., T, head_dim, ...) is exactly
  * mqa_prefill_ex(..., T, T, head_dim, head_dim, ...).
  */

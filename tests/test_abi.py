@@ -87,10 +87,11 @@ def test_f16_is_accepted_where_supported():
 
 
 def test_prefill_workspace_size():
-    # bf16: K and a transposed V as whole 32-key tiles
-    # (d = 512: each 1 KB K row carries 16 bytes of padding)
+    # bf16: a transposed V as whole 32-key tiles, and at d = 512 the K tile
+    # too (each 1 KB K row carrying 16 bytes of padding); narrower K rows are
+    # copied from K itself
     assert lib.mqa_prefill_workspace_size(2, 16, 1, 4096, 512, BF16) == 2 * 1 * 4096 * (1040 + 1024)
-    assert lib.mqa_prefill_workspace_size(1, 8, 2, 33, 128, BF16) == 2 * 1 * 2 * 64 * 128 * 2
+    assert lib.mqa_prefill_workspace_size(1, 8, 2, 33, 128, BF16) == 1 * 2 * 64 * 128 * 2
     assert lib.mqa_prefill_workspace_size(1, 16, 1, 128, 512, F32) == 0
 
 
@@ -125,8 +126,8 @@ def test_prefill_ex_empty_and_noncausal_shapes():
 
 
 def test_prefill_ex_workspace_size():
-    # K tile (d_qk) and transposed V tile (d_v) per 32 keys of T_kv
-    assert lib.mqa_prefill_ex_workspace_size(1, 128, 128, 100, 8192, 192, 128, BF16) == 128 * 8192 * (192 + 128) * 2
+    # transposed V tile (d_v) per 32 keys of T_kv (plus the padded K tile at 512)
+    assert lib.mqa_prefill_ex_workspace_size(1, 128, 128, 100, 8192, 192, 128, BF16) == 128 * 8192 * 128 * 2
     assert lib.mqa_prefill_ex_workspace_size(2, 16, 1, 7, 33, 512, 512, BF16) == 2 * 1 * 64 * (1040 + 1024)
     assert lib.mqa_prefill_ex_workspace_size(1, 128, 128, 100, 8192, 192, 128, F32) == 0
     # the square entry point is the general one with T_q = T_kv, d_v = d_qk
