@@ -177,7 +177,7 @@ int mla_decode_absorbed(const void* q_abs, const void* kv_cache, const int32_t* 
     if (!aligned16(q_abs) || !aligned16(kv_cache) || !aligned16(out) || ((uintptr_t)seq_lens & 3u) ||
         (lse && ((uintptr_t)lse & 3u)))
         return MQA_ERR_INVALID_ARG;
-    if (dtype != MQA_DTYPE_BF16 || !valid_out(dtype, out_dtype)) return MQA_ERR_UNSUPPORTED;
+    if (!is16(dtype) || !valid_out(dtype, out_dtype)) return MQA_ERR_UNSUPPORTED;
     if (H % 16 != 0 || H > 128) return MQA_ERR_UNSUPPORTED;
     if (max_len == 0) return MQA_ERR_INVALID_ARG;
     // one sequence's latent cache is addressed with 32-bit byte offsets
@@ -189,6 +189,7 @@ int mla_decode_absorbed(const void* q_abs, const void* kv_cache, const int32_t* 
     mqa::MlaArgs a;
     a.q = q_abs; a.kv = kv_cache; a.seq_lens = seq_lens; a.indices = nullptr; a.topk = 0; a.out = out; a.lse = lse;
     a.B = B; a.H = H; a.max_len = max_len; a.scale = scale; a.out_f32 = out_dtype == MQA_DTYPE_F32;
+    a.f16 = dtype == MQA_DTYPE_F16;
     a.part_o = (float*)workspace;
     a.part_ml = (float*)workspace + (size_t)B * H * plan.n_split * 512;
     a.plan = plan; a.stream = (hipStream_t)stream;
@@ -212,7 +213,7 @@ int mla_decode_sparse(const void* q_abs, const void* kv_cache, const int32_t* in
     if (!aligned16(q_abs) || !aligned16(kv_cache) || !aligned16(out) || ((uintptr_t)indices & 3u) ||
         (lse && ((uintptr_t)lse & 3u)))
         return MQA_ERR_INVALID_ARG;
-    if (dtype != MQA_DTYPE_BF16 || !valid_out(dtype, out_dtype)) return MQA_ERR_UNSUPPORTED;
+    if (!is16(dtype) || !valid_out(dtype, out_dtype)) return MQA_ERR_UNSUPPORTED;
     if (H % 16 != 0 || H > 128) return MQA_ERR_UNSUPPORTED;
     // one sequence's latent cache is addressed with 32-bit byte offsets
     if ((size_t)max_len * 576 * 2 > 0xFFFFFFFFull) return MQA_ERR_UNSUPPORTED;
@@ -223,6 +224,7 @@ int mla_decode_sparse(const void* q_abs, const void* kv_cache, const int32_t* in
     mqa::MlaArgs a;
     a.q = q_abs; a.kv = kv_cache; a.seq_lens = nullptr; a.indices = indices; a.topk = topk; a.out = out; a.lse = lse;
     a.B = B; a.H = H; a.max_len = max_len; a.scale = scale; a.out_f32 = out_dtype == MQA_DTYPE_F32;
+    a.f16 = dtype == MQA_DTYPE_F16;
     a.part_o = (float*)workspace;
     a.part_ml = (float*)workspace + (size_t)B * H * plan.n_split * 512;
     a.plan = plan; a.stream = (hipStream_t)stream;

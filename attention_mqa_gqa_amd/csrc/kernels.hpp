@@ -75,6 +75,7 @@ struct MlaArgs {
     int B, H, max_len;
     float scale;
     bool out_f32;
+    bool f16;        // fp16 inputs (and fp16 output unless out_f32); else bf16
     float* part_o;   // [B*H*n_split, 512]
     float* part_ml;  // [B*H*n_split, 2]
     DecodePlan plan;

@@ -54,7 +54,7 @@ constexpr int kMaxSparseChunk = 2048;                            // list entries
 
 // SPARSE = false: sequence b's rows are 0 .. seq_lens[b]-1 (indices unused).
 // SPARSE = true:  its rows are indices[b, 0 .. topk-1] (seq_lens unused).
-template <bool SPARSE>
+template <bool SPARSE, bool F16>
 __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
     const bf16* __restrict__ Qa, const bf16* __restrict__ KV, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ indices, float* __restrict__ part_o, float* __restrict__ part_ml, int H,
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
             between(ks);
             const bf16x8 a = abuf[ks % PF];
             if (ks + PF < KS) abuf[ks % PF] = kread(st, ks + PF);
-            sc = mfma_32x32x16(a, qb[ks], sc);
+            sc = mfma_32x32x16_t<F16>(a, qb[ks], sc);
         }
         sched_reads_ahead<PF, KS - PF>();
         return sc;
@@ -254,8 +254,8 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
             l_run += p[i];
         }
         u32x2 pk;
-        pk.x = pack_bf16x2(p[0], p[1]);
-        pk.y = pack_bf16x2(p[2], p[3]);
+        pk.x = pack2_t<F16>(p[0], p[1]);
+        pk.y = pack2_t<F16>(p[2], p[3]);
         char* pl = pbuf + (tile & 1) * kPB + head * 64 + 8 * h2;
         *(u32x2*)(pl + ((c ^ layout::ptile_swz(head)) * 16)) = pk;
     };
@@ -308,7 +308,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) mfma_32x32x16_acc(va[stp % 3], pb[stp / MT][nt], o[stp % MT][nt]);
+            for (int nt = 0; nt < NT; ++nt) mfma_32x32x16_acc_t<F16>(va[stp % 3], pb[stp / MT][nt], o[stp % MT][nt]);
             between(stp);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -384,7 +384,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
                     }
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) mfma_32x32x16_acc(va[stp % 3], pb[stp / MT][nt], o[stp % MT][nt]);
+                    for (int nt = 0; nt < NT; ++nt) mfma_32x32x16_acc_t<F16>(va[stp % 3], pb[stp / MT][nt], o[stp % MT][nt]);
                     if (stp == 1) sm_max(sn, it + 1);
                     if (stp >= 2 && stp < 6) sm_exp(sn, it + 1, stp - 2);
                     if (stp == 6) sm_alpha(it + 1);
@@ -465,21 +465,27 @@ DecodePlan mla_sparse_plan(int B, int topk) {
     return p;
 }
 
-hipError_t mla_launch(const MlaArgs& a) {
+template <bool SPARSE, bool F16>
+static void mla_kernel_launch(const MlaArgs& a) {
     const dim3 grid(a.plan.n_split, a.B);
-    if (a.indices != nullptr)
-        hipLaunchKernelGGL(mla_decode_kernel<true>, grid, dim3(kNW * 64), 0, a.stream, (const bf16*)a.q,
-                           (const bf16*)a.kv, (const int32_t*)nullptr, a.indices, a.part_o, a.part_ml, a.H,
-                           a.max_len, a.topk, a.plan.chunk, a.plan.n_split, a.scale * kLog2e);
-    else
-        hipLaunchKernelGGL(mla_decode_kernel<false>, grid, dim3(kNW * 64), 0, a.stream, (const bf16*)a.q,
-                           (const bf16*)a.kv, a.seq_lens, (const int32_t*)nullptr, a.part_o, a.part_ml, a.H,
-                           a.max_len, 0, a.plan.chunk, a.plan.n_split, a.scale * kLog2e);
+    hipLaunchKernelGGL((mla_decode_kernel<SPARSE, F16>), grid, dim3(kNW * 64), 0, a.stream, (const bf16*)a.q,
+                       (const bf16*)a.kv, SPARSE ? (const int32_t*)nullptr : a.seq_lens,
+                       SPARSE ? a.indices : (const int32_t*)nullptr, a.part_o, a.part_ml, a.H, a.max_len,
+                       SPARSE ? a.topk : 0, a.plan.chunk, a.plan.n_split, a.scale * kLog2e);
+}
+
+hipError_t mla_launch(const MlaArgs& a) {
+    const bool sparse = a.indices != nullptr;
+    if (sparse) {
+        if (a.f16) mla_kernel_launch<true, true>(a); else mla_kernel_launch<true, false>(a);
+    } else {
+        if (a.f16) mla_kernel_launch<false, true>(a); else mla_kernel_launch<false, false>(a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // sparse: every split of every sequence wrote a partial (seq_lens = null)
-    return merge_launch(a.part_o, a.part_ml, a.indices != nullptr ? nullptr : a.seq_lens, a.out, a.lse, a.B, a.H,
-                        a.max_len, kDC, a.plan.chunk, a.plan.n_split, a.out_f32, false, a.stream);
+    return merge_launch(a.part_o, a.part_ml, sparse ? nullptr : a.seq_lens, a.out, a.lse, a.B, a.H, a.max_len, kDC,
+                        a.plan.chunk, a.plan.n_split, a.out_f32, a.f16, a.stream);
 }
 
 }  // namespace mqa

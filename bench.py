@@ -19,6 +19,9 @@ workload, inputs already resident in HBM:
   * mqa_prefill          the first workload with fp16 inputs and output
 all bf16 in (but the last), fp32 accumulation, 16-bit out.
 
+W untimed warm-up steps run first, extended (at most 400 steps) until they
+have kept the GPU busy for 1 s: a fresh device runs its first ~25 calls
+20-25 % slower while its clocks settle.  Then exactly K steps are timed.
 Every call is bracketed with HIP events on the stream it is launched on.
 The headline `value` is the causal MQA prefill TFLOP/s (visible query/key
 pairs only, 2 (d_qk + d_v) flops per pair); the other workloads sit beside it, each
@@ -316,8 +319,13 @@ def main():
             if events is not None:
                 events[name][1].record(stream)
 
-    for _ in range(args.warmup):
+    t_w = time.perf_counter()
+    n_w = 0
+    while n_w < args.warmup or (time.perf_counter() - t_w < 1.0 and n_w < 400):
         step()
+        n_w += 1
+        if n_w >= args.warmup:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     evs = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
            for _ in range(args.steps)]
@@ -361,6 +369,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_run": n_w,
         "ms_per_step": round(wall * 1e3 / args.steps, 4),
         "higher_is_better": True,
         "scaling": "weak",

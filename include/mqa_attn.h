@@ -180,7 +180,7 @@ int mqa_decode(const void* q, const void* k_cache, const void* v_cache,
  *   lse [B, H] fp32 or NULL.
  *   scale: normally 1/sqrt(128 + 64), the original per-head q.k width;
  *          finite and > 0.
- * Supported: dtype BF16, out_dtype BF16 or F32, H a multiple of 16, H <= 128.
+ * Supported: dtype BF16 or F16, out_dtype the same or F32, H a multiple of 16, H <= 128.
  * Workspace: `mla_decode_workspace_size()` bytes.
  */
 size_t mla_decode_workspace_size(int B, int H, int max_len);
@@ -204,7 +204,7 @@ int mla_decode_absorbed(const void* q_abs, const void* kv_cache, const int32_t* 
  *   rows; a row listed twice enters the softmax twice.  A sequence with no
  *   valid entry gets out = 0 and lse = -inf.
  *   lse [B, H] fp32 or NULL.  scale as for mla_decode_absorbed.
- * Supported: dtype BF16, out_dtype BF16 or F32, H a multiple of 16, H <= 128,
+ * Supported: dtype BF16 or F16, out_dtype the same or F32, H a multiple of 16, H <= 128,
  *   topk >= 1 (topk <= 0 is MQA_ERR_INVALID_ARG).
  * Workspace: `mla_decode_sparse_workspace_size()` bytes (chunk partials of
  *   the index list).

@@ -171,8 +171,10 @@ def test_mla_rejections():
     assert _mla(H=24) == UNSUPPORTED
     assert _mla(H=256) == UNSUPPORTED
     assert _mla(dt=F32) == UNSUPPORTED
-    assert _mla(dt=F16, dout=F16) == UNSUPPORTED          # MLA: bf16 only
-    assert _mla(dt=BF16, dout=F16) == UNSUPPORTED
+    assert _mla(dt=F16, dout=F16, ws=None) == WORKSPACE   # fp16 accepted (validation only)
+    assert _mla(dt=F16, dout=F32, ws=None) == WORKSPACE
+    assert _mla(dt=BF16, dout=F16) == UNSUPPORTED          # 16-bit out = the input type
+    assert _mla(dt=F16, dout=BF16) == UNSUPPORTED
     assert _mla(ws=None) == WORKSPACE
     need = lib.mla_decode_workspace_size(32, 128, 32768)
     assert _mla(wsb=need - 1) == WORKSPACE
@@ -192,6 +194,8 @@ def test_mla_sparse_rejections():
     assert _sparse(scale=float("nan")) == INVALID
     assert _sparse(H=24) == UNSUPPORTED
     assert _sparse(dt=F32) == UNSUPPORTED
+    assert _sparse(dt=F16, dout=F16, ws=None) == WORKSPACE
+    assert _sparse(dt=BF16, dout=F16) == UNSUPPORTED
     assert _sparse(ws=None) == WORKSPACE
     need = lib.mla_decode_sparse_workspace_size(32, 128, 2048)
     assert need > 0 and need % (32 * 128 * (512 + 2) * 4) == 0

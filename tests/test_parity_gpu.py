@@ -404,6 +404,40 @@ def test_mla_small(torch, mqa, B, H, L, lengths, odt):
     assert _maxerr(host(lse), ref_lse) <= BF16_TOL
 
 
+MLA_F16 = [
+    # B, H, L_max, lengths, topk (0: dense), out dtype
+    (3, 128, 1500, [1500, 31, 777], 0, "f16"),
+    (2, 64, 600, [600, 65], 0, "f32"),
+    (2, 128, 3000, [3000, 200], 512, "f16"),   # sparse: 512 listed rows (200 for the short sequence)
+]
+
+
+@pytest.mark.parametrize("B,H,L,lengths,topk,odt", MLA_F16)
+def test_mla_f16(torch, mqa, B, H, L, lengths, topk, odt):
+    """fp16 queries and latent cache (dense and sparse), fp16 or fp32 out."""
+    _say(f"mla f16 B{B} H{H} L{L} lens={lengths} topk={topk} out={odt}")
+    q, kv, sl = mla_inputs(B, H, L, 576, "f16", seed=8, lengths=lengths)
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    out_dtype = torch.float32 if odt == "f32" else torch.float16
+    scale = 1 / math.sqrt(192)
+    if topk:
+        idx = draw_topk(B, sl, topk, seed=8)
+        out = mqa.mla_decode_sparse(dev(torch, q), dev(torch, kv), torch.from_numpy(idx).cuda(), lse=lse,
+                                    out_dtype=out_dtype)
+        ref, ref_lse = oracle.mla_sparse_ref(q.f32(), kv.f32(), idx, scale)
+    else:
+        out = mqa.mla_decode_absorbed(dev(torch, q), dev(torch, kv), torch.from_numpy(sl).cuda(), lse=lse,
+                                      out_dtype=out_dtype)
+        ref, ref_lse = oracle.mla_absorbed_ref(q.f32(), kv.f32(), sl, scale)
+    torch.cuda.synchronize()
+    assert out.dtype == out_dtype
+    assert np.all(np.isfinite(host(out)))
+    err = _maxerr(host(out), ref)
+    _say(f"  max |err| {err:.2e}")
+    assert err <= F16_TOL
+    assert _maxerr(host(lse), ref_lse) <= F16_TOL
+
+
 def test_mla_full_size(torch, mqa):
     """MLA absorbed decode batch 32, H=128, context 32768, scale 1/sqrt(192)."""
     _say("mla full B32 H128 L32768")
