@@ -241,9 +241,10 @@ int mla_absorb_query(const void* q_nope, const void* q_rope, const void* w_uk, c
     if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(w_uk) || !aligned16(q_abs) ||
         ((uintptr_t)cos_t & 3u) || ((uintptr_t)sin_t & 3u))
         return MQA_ERR_INVALID_ARG;
-    if (dtype != MQA_DTYPE_BF16) return MQA_ERR_UNSUPPORTED;
+    if (!is16(dtype)) return MQA_ERR_UNSUPPORTED;
     clear_stale_error();
-    return hip_status(mqa::mla_absorb_launch(q_nope, q_rope, w_uk, cos_t, sin_t, q_abs, B, H, (hipStream_t)stream));
+    return hip_status(mqa::mla_absorb_launch(q_nope, q_rope, w_uk, cos_t, sin_t, q_abs, B, H, dtype == MQA_DTYPE_F16,
+                                             (hipStream_t)stream));
 }
 
 int mla_cache_append(const void* c_kv, const void* k_pe, const float* cos_t, const float* sin_t,
@@ -255,10 +256,10 @@ int mla_cache_append(const void* c_kv, const void* k_pe, const float* cos_t, con
     if (!aligned16(c_kv) || !aligned16(k_pe) || !aligned16(kv_cache) || ((uintptr_t)cos_t & 3u) ||
         ((uintptr_t)sin_t & 3u) || ((uintptr_t)positions & 3u))
         return MQA_ERR_INVALID_ARG;
-    if (dtype != MQA_DTYPE_BF16) return MQA_ERR_UNSUPPORTED;
+    if (!is16(dtype)) return MQA_ERR_UNSUPPORTED;
     clear_stale_error();
     return hip_status(mqa::mla_cache_append_launch(c_kv, k_pe, cos_t, sin_t, positions, kv_cache, B, max_len,
-                                                   (hipStream_t)stream));
+                                                   dtype == MQA_DTYPE_F16, (hipStream_t)stream));
 }
 
 int mla_output_project(const void* o_lat, const void* w_uv, void* out, int B, int H, int dtype, int out_dtype,
@@ -268,10 +269,10 @@ int mla_output_project(const void* o_lat, const void* w_uv, void* out, int B, in
     if (B == 0) return MQA_OK;
     if (!o_lat || !w_uv || !out) return MQA_ERR_INVALID_ARG;
     if (!aligned16(o_lat) || !aligned16(w_uv) || !aligned16(out)) return MQA_ERR_INVALID_ARG;
-    if (dtype != MQA_DTYPE_BF16 || !valid_out(dtype, out_dtype)) return MQA_ERR_UNSUPPORTED;
+    if (!is16(dtype) || !valid_out(dtype, out_dtype)) return MQA_ERR_UNSUPPORTED;
     clear_stale_error();
     return hip_status(mqa::mla_out_proj_launch(o_lat, w_uv, out, B, H, out_dtype == MQA_DTYPE_F32,
-                                               (hipStream_t)stream));
+                                               dtype == MQA_DTYPE_F16, (hipStream_t)stream));
 }
 
 }  // extern "C"

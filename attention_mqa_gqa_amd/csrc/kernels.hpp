@@ -85,12 +85,13 @@ struct MlaArgs {
 hipError_t mla_launch(const MlaArgs& a);
 
 // The steps either side of absorbed MLA decode (d_c 512, d_nope 128, d_R 64, d_v 128).
+// f16: fp16 tensors (else bf16); out_f32: fp32 output (else the input type)
 hipError_t mla_absorb_launch(const void* q_nope, const void* q_rope, const void* w_uk, const float* cosv,
-                             const float* sinv, void* q_abs, int B, int H, hipStream_t stream);
+                             const float* sinv, void* q_abs, int B, int H, bool f16, hipStream_t stream);
 hipError_t mla_cache_append_launch(const void* c_kv, const void* k_pe, const float* cosv, const float* sinv,
-                                   const int32_t* positions, void* kv_cache, int B, int max_len,
+                                   const int32_t* positions, void* kv_cache, int B, int max_len, bool f16,
                                    hipStream_t stream);
-hipError_t mla_out_proj_launch(const void* o_lat, const void* w_uv, void* out, int B, int H, bool out_f32,
+hipError_t mla_out_proj_launch(const void* o_lat, const void* w_uv, void* out, int B, int H, bool out_f32, bool f16,
                                hipStream_t stream);
 
 // LSE merge of split partials (shared by both decode paths).

@@ -33,16 +33,31 @@ constexpr int kDr = 64;     // RoPE part
 constexpr int kDv = 128;    // value head dim
 constexpr int kDq = kDc + kDr;
 
+// One 16-bit element (bf16, or fp16 if F16; bf16 is the bit container) to
+// fp32, and back with round to nearest even.
+template <bool F16>
+__device__ __forceinline__ float ld16f(const bf16* p) {
+    if constexpr (F16) return (float)__builtin_bit_cast(_Float16, *(const uint16_t*)p);
+    else return (float)*p;
+}
+template <bool F16>
+__device__ __forceinline__ bf16 st16f(float v) {
+    if constexpr (F16) return __builtin_bit_cast(bf16, (_Float16)v);
+    else return (bf16)v;
+}
+
 // RoPE of one element: x d (of kDr) rotated by (cos, sin) of its position,
 // rotate-half form: partner -x[d + 32] for the first half, x[d - 32] after.
+template <bool F16>
 __device__ __forceinline__ float rope_elem(const bf16* x, int d, const float* cs, const float* sn) {
-    const float xv = (float)x[d];
-    const float partner = d < kDr / 2 ? -(float)x[d + kDr / 2] : (float)x[d - kDr / 2];
+    const float xv = ld16f<F16>(x + d);
+    const float partner = d < kDr / 2 ? -ld16f<F16>(x + d + kDr / 2) : ld16f<F16>(x + d - kDr / 2);
     return xv * cs[d] + partner * sn[d];
 }
 }  // namespace
 
 // grid (H, kDc / 128): workgroup = one head, 128 latent dims (32 per wave).
+template <bool F16>
 __global__ __launch_bounds__(256) void mla_absorb_kernel(const bf16* __restrict__ q_nope,
                                                          const bf16* __restrict__ q_rope,
                                                          const bf16* __restrict__ w_uk,
@@ -74,15 +89,15 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const bf16* __restrict_
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const u32x4 v = ldg16(qrow + 16 * ks);
-            acc = mfma_32x32x16(wa[ks], __builtin_bit_cast(bf16x8, ok ? v : u32x4{0, 0, 0, 0}), acc);
+            acc = mfma_32x32x16_t<F16>(wa[ks], __builtin_bit_cast(bf16x8, ok ? v : u32x4{0, 0, 0, 0}), acc);
         }
         // accumulator i: latent row c0 + 8(i/4) + 4 h2 + i%4, sequence b
         __syncthreads();                         // the previous step's stores have read the stage
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             u32x2 pk;
-            pk.x = pack_bf16x2(acc[4 * q + 0], acc[4 * q + 1]);
-            pk.y = pack_bf16x2(acc[4 * q + 2], acc[4 * q + 3]);
+            pk.x = pack2_t<F16>(acc[4 * q + 0], acc[4 * q + 1]);
+            pk.y = pack2_t<F16>(acc[4 * q + 2], acc[4 * q + 3]);
             *(u32x2*)&stage[n][32 * w + 8 * q + 4 * h2] = pk;
         }
         __syncthreads();
@@ -100,13 +115,14 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const bf16* __restrict_
 #pragma unroll 2
     for (int e = (int)threadIdx.x; e < B * kRd; e += 256) {
         const int b = e / kRd, d = kRd * blockIdx.y + e % kRd;
-        const float y = rope_elem(q_rope + ((size_t)b * H + h) * kDr, d, cosv + (size_t)b * kDr,
-                                  sinv + (size_t)b * kDr);
-        q_abs[((size_t)b * H + h) * kDq + kDc + d] = (bf16)y;
+        const float y = rope_elem<F16>(q_rope + ((size_t)b * H + h) * kDr, d, cosv + (size_t)b * kDr,
+                                       sinv + (size_t)b * kDr);
+        q_abs[((size_t)b * H + h) * kDq + kDc + d] = st16f<F16>(y);
     }
 }
 
 // grid (B): row positions[b] of sequence b's cache = [c_kv | RoPE(k_pe)].
+template <bool F16>
 __global__ __launch_bounds__(64) void mla_cache_append_kernel(const bf16* __restrict__ c_kv,
                                                               const bf16* __restrict__ k_pe,
                                                               const float* __restrict__ cosv,
@@ -119,12 +135,12 @@ __global__ __launch_bounds__(64) void mla_cache_append_kernel(const bf16* __rest
     if (pos < 0 || pos >= max_len) return;
     bf16* row = kv_cache + ((size_t)b * max_len + pos) * kDq;
     *(u32x4*)(row + 8 * t) = ldg16(c_kv + (size_t)b * kDc + 8 * t);      // 64 lanes x 8 = 512
-    row[kDc + t] = (bf16)rope_elem(k_pe + (size_t)b * kDr, t, cosv + (size_t)b * kDr, sinv + (size_t)b * kDr);
+    row[kDc + t] = st16f<F16>(rope_elem<F16>(k_pe + (size_t)b * kDr, t, cosv + (size_t)b * kDr, sinv + (size_t)b * kDr));
 }
 
 // grid (H, ceil(B / 16)): workgroup = one head, 16 sequences, all 128 value
 // dims; wave w sums latent dims 128 w .. 128 w + 127.
-template <bool OUT_F32>
+template <bool OUT_F32, bool F16>
 __global__ __launch_bounds__(256) void mla_out_proj_kernel(const bf16* __restrict__ o_lat,
                                                            const bf16* __restrict__ w_uv, void* __restrict__ out,
                                                            int B, int H) {
@@ -165,7 +181,7 @@ __global__ __launch_bounds__(256) void mla_out_proj_kernel(const bf16* __restric
             u32x2 a;
             a.x = perm(r[st][1][wd], r[st][0][wd], sel);
             a.y = perm(r[st][3][wd], r[st][2][wd], sel);
-            acc[t] = mfma_16x16x16(a, bop[st], acc[t]);
+            acc[t] = mfma_16x16x16_t<F16>(a, bop[st], acc[t]);
         }
     }
     // acc[t][i]: value dim 8(4g + i) + t, sequence b0 + m
@@ -180,34 +196,46 @@ __global__ __launch_bounds__(256) void mla_out_proj_kernel(const bf16* __restric
         const float y = red[0][bb][d] + red[1][bb][d] + red[2][bb][d] + red[3][bb][d];
         const size_t o = ((size_t)(b0 + bb) * H + h) * kDv + d;
         if constexpr (OUT_F32) ((float*)out)[o] = y;
-        else ((bf16*)out)[o] = (bf16)y;
+        else ((bf16*)out)[o] = st16f<F16>(y);
     }
 }
 
 hipError_t mla_absorb_launch(const void* q_nope, const void* q_rope, const void* w_uk, const float* cosv,
-                             const float* sinv, void* q_abs, int B, int H, hipStream_t stream) {
-    hipLaunchKernelGGL(mla_absorb_kernel, dim3(H, kDc / 128), dim3(256), 0, stream, (const bf16*)q_nope,
-                       (const bf16*)q_rope, (const bf16*)w_uk, cosv, sinv, (bf16*)q_abs, B, H);
+                             const float* sinv, void* q_abs, int B, int H, bool f16, hipStream_t stream) {
+    const dim3 grid(H, kDc / 128);
+    if (f16)
+        hipLaunchKernelGGL(mla_absorb_kernel<true>, grid, dim3(256), 0, stream, (const bf16*)q_nope,
+                           (const bf16*)q_rope, (const bf16*)w_uk, cosv, sinv, (bf16*)q_abs, B, H);
+    else
+        hipLaunchKernelGGL(mla_absorb_kernel<false>, grid, dim3(256), 0, stream, (const bf16*)q_nope,
+                           (const bf16*)q_rope, (const bf16*)w_uk, cosv, sinv, (bf16*)q_abs, B, H);
     return hipGetLastError();
 }
 
 hipError_t mla_cache_append_launch(const void* c_kv, const void* k_pe, const float* cosv, const float* sinv,
-                                   const int32_t* positions, void* kv_cache, int B, int max_len,
+                                   const int32_t* positions, void* kv_cache, int B, int max_len, bool f16,
                                    hipStream_t stream) {
-    hipLaunchKernelGGL(mla_cache_append_kernel, dim3(B), dim3(64), 0, stream, (const bf16*)c_kv, (const bf16*)k_pe,
-                       cosv, sinv, positions, (bf16*)kv_cache, max_len);
+    if (f16)
+        hipLaunchKernelGGL(mla_cache_append_kernel<true>, dim3(B), dim3(64), 0, stream, (const bf16*)c_kv,
+                           (const bf16*)k_pe, cosv, sinv, positions, (bf16*)kv_cache, max_len);
+    else
+        hipLaunchKernelGGL(mla_cache_append_kernel<false>, dim3(B), dim3(64), 0, stream, (const bf16*)c_kv,
+                           (const bf16*)k_pe, cosv, sinv, positions, (bf16*)kv_cache, max_len);
     return hipGetLastError();
 }
 
-hipError_t mla_out_proj_launch(const void* o_lat, const void* w_uv, void* out, int B, int H, bool out_f32,
+hipError_t mla_out_proj_launch(const void* o_lat, const void* w_uv, void* out, int B, int H, bool out_f32, bool f16,
                                hipStream_t stream) {
     const dim3 grid(H, (B + 15) / 16);
-    if (out_f32)
-        hipLaunchKernelGGL(mla_out_proj_kernel<true>, grid, dim3(256), 0, stream, (const bf16*)o_lat,
-                           (const bf16*)w_uv, out, B, H);
-    else
-        hipLaunchKernelGGL(mla_out_proj_kernel<false>, grid, dim3(256), 0, stream, (const bf16*)o_lat,
-                           (const bf16*)w_uv, out, B, H);
+#define MQA_OUT_PROJ(O, F) \
+    hipLaunchKernelGGL((mla_out_proj_kernel<O, F>), grid, dim3(256), 0, stream, (const bf16*)o_lat, (const bf16*)w_uv, \
+                       out, B, H)
+    if (f16) {
+        if (out_f32) MQA_OUT_PROJ(true, true); else MQA_OUT_PROJ(false, true);
+    } else {
+        if (out_f32) MQA_OUT_PROJ(true, false); else MQA_OUT_PROJ(false, false);
+    }
+#undef MQA_OUT_PROJ
     return hipGetLastError();
 }
 

@@ -231,8 +231,9 @@ int mla_decode_sparse(const void* q_abs, const void* kv_cache, const int32_t* in
  *   RoPE(x) = x * cos + [-x[32:64] | x[0:32]] * sin,
  * with cos, sin fp32 [B, 64] the rotary factors of each sequence's position
  * (the caller builds them, as a model's position embeddings).
- * dtype BF16 only (MQA_ERR_UNSUPPORTED otherwise); every pointer a device
- * pointer, 16-byte aligned (cos / sin / positions 4-byte aligned).
+ * dtype BF16 or F16 for every 16-bit tensor of the call (MQA_ERR_UNSUPPORTED
+ * otherwise); every pointer a device pointer, 16-byte aligned (cos / sin /
+ * positions 4-byte aligned).
  *
  * mla_absorb_query: q_nope [B, H, 128], q_rope [B, H, 64],
  *   w_uk [H, 512, 128] (per head: latent x nope) ->
@@ -243,7 +244,7 @@ int mla_decode_sparse(const void* q_abs, const void* kv_cache, const int32_t* in
  *   device; a position outside [0, max_len) writes nothing.
  * mla_output_project: o_lat [B, H, 512] (mla_decode_absorbed's output),
  *   w_uv [H, 512, 128] (per head: latent x value) ->
- *   out [B, H, 128] = o_lat[b, h] W_UV[h]; out_dtype BF16 or F32.
+ *   out [B, H, 128] = o_lat[b, h] W_UV[h]; out_dtype = dtype or F32.
  */
 int mla_absorb_query(const void* q_nope, const void* q_rope, const void* w_uk,
                      const float* cos_t, const float* sin_t, void* q_abs,

@@ -211,7 +211,7 @@ def test_mla_step_rejections():
     assert ab(w=None) == INVALID
     assert ab(c=ctypes.c_void_p(4098)) == INVALID
     assert ab(o=MIS) == INVALID
-    assert ab(dt=F16) == UNSUPPORTED
+    assert ab(dt=F32) == UNSUPPORTED                       # 16-bit only (bf16, fp16)
     assert ab(B=0, qn=None) == OK
     ap = lambda **k: lib.mla_cache_append(k.get("c", P), k.get("k", P), P, P, k.get("pos", P), k.get("kv", P),
                                           k.get("B", 4), k.get("L", 100), k.get("dt", BF16), None)
@@ -225,6 +225,7 @@ def test_mla_step_rejections():
     assert op(H=-1) == INVALID
     assert op(out=None) == INVALID
     assert op(dt=BF16, dout=F16) == UNSUPPORTED
+    assert op(dt=F16, dout=BF16) == UNSUPPORTED
     assert op(dt=F32, dout=F32) == UNSUPPORTED
     assert op(B=0, o=None) == OK
 

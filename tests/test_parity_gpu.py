@@ -532,6 +532,43 @@ def test_mla_output_project(torch, mqa, B, odt):
     assert _maxerr(host(out), ref) <= (F32_TOL * 100 if odt == "f32" else BF16_TOL)
 
 
+def test_mla_step_f16(torch, mqa):
+    """The three step kernels on fp16 tensors: absorption + RoPE, cache
+    append (latent bits copied, RoPE part rounded to fp16), W_UV with fp16
+    and fp32 output."""
+    _say("mla step fp16: absorb B9 H128, append B3 L16, W_UV B20")
+    B, H = 9, 128
+    qn, qr, ckv, kpe, wuk, wuv = mla_step_inputs(B, H, "f16", seed=25)
+    pos = np.random.default_rng(25).integers(0, 40000, size=B)
+    dc, ds, c, s_ = _cs(torch, pos)
+    q_abs = mqa.mla_absorb_query(dev(torch, qn), dev(torch, qr), dev(torch, wuk), dc, ds)
+    torch.cuda.synchronize()
+    assert q_abs.dtype == torch.float16
+    ref = oracle.absorb_query(qn.f32(), oracle.rope_ref(qr.f32(), c[:, None], s_[:, None]), wuk.f32())
+    assert _maxerr(host(q_abs), ref) <= F16_TOL
+
+    L = 16
+    p3 = np.array([0, 15, 7], dtype=np.int32)
+    dc3, ds3, c3, s3 = _cs(torch, p3)
+    cache = torch.zeros((3, L, 576), dtype=torch.float16, device="cuda")
+    mqa.mla_cache_append(cache, dev(torch, ckv)[:3].contiguous(), dev(torch, kpe)[:3].contiguous(), dc3, ds3,
+                         torch.from_numpy(p3).cuda())
+    torch.cuda.synchronize()
+    got = host(cache)
+    rot = oracle.rope_ref(kpe.f32()[:3], c3, s3)
+    for b in range(3):
+        row = got[b, p3[b]]
+        assert np.array_equal(row[:512], ckv.f32()[b])
+        assert np.max(np.abs(row[512:] - rot[b])) <= 2 ** -10 * max(1.0, np.max(np.abs(rot[b])))
+
+    o_lat, _, _ = mla_inputs(20, H, 1, 512, "f16", seed=25)
+    for out_dtype in (torch.float16, torch.float32):
+        out = mqa.mla_output_project(dev(torch, o_lat), dev(torch, wuv), out_dtype=out_dtype)
+        torch.cuda.synchronize()
+        assert out.dtype == out_dtype
+        assert _maxerr(host(out), oracle.output_project(o_lat.f32(), wuv.f32())) <= F16_TOL
+
+
 def test_mla_decode_step_end_to_end(torch, mqa):
     """Cache built token by token with mla_cache_append, then one step:
     mla_absorb_query -> mla_decode_absorbed -> mla_output_project, against
