@@ -128,7 +128,7 @@ int mqa_prefill(const void* q, const void* k, const void* v, void* out, float* l
  *   expanded and decode absorbed; dimensions as in walkerchi.com "Full 路线"
  *   §四 4.2).
  * Supported: everything mqa_prefill supports (d_qk == d_v, as listed there),
- *   plus (d_qk, d_v) = (192, 128) with any G <= 256 (16-bit) or any G (fp32).
+ *   plus (d_qk, d_v) = (192, 128) with any G <= 128 (16-bit) or any G (fp32).
  *   T_q == 0 or B == 0 is an empty call; T_kv == 0 with T_q > 0 is rejected.
  * Workspace (16-bit inputs): `mqa_prefill_ex_workspace_size()` bytes =
  *   B * Hkv * ceil(T_kv/32) * 32 * (k + d_v) * 2, k = d_qk + 8 when
