@@ -59,9 +59,13 @@ __global__ __launch_bounds__(256) void kv_pack_kernel(const bf16* __restrict__ K
     const bf16* vsrc = V + bh * (size_t)T * DV;
     char* kdst = (char*)KVt + (bh * n_tiles + tile) * (size_t)(KTILE_B + 2 * TILE_V);
     bf16* vdst = (bf16*)(kdst + KTILE_B);
+    // blockIdx.z: 0 packs the K tile (1 KB rows only), 1 the V^T tile (a
+    // grid of depth 1 packs only V^T)
+    const int part = KPAD ? (int)blockIdx.z : 1;
     // K tile: chunk position p of row position kk holds global chunk
     // p ^ swz(kk) of key kk, or (1 KB rows) chunk p of key padded_row_pos(kk)
-    for (int q = threadIdx.x; KPAD && q < KT * ROW_CHUNKS; q += 256) {
+#pragma unroll 8
+    for (int q = threadIdx.x; part == 0 && q < KT * ROW_CHUNKS; q += 256) {
         const int kk = q / ROW_CHUNKS;
         const int p = q % ROW_CHUNKS;
         const int c = KPAD ? p : (p ^ layout::swz32(kk, ROW_CHUNKS));
@@ -70,7 +74,7 @@ __global__ __launch_bounds__(256) void kv_pack_kernel(const bf16* __restrict__ K
         *(u32x4*)(kdst + kk * KROW_B + p * 16) = val;
     }
     // V^T tile: 8x8 blocks transposed with byte permutes
-    for (int blk = threadIdx.x; blk < NB; blk += 256) {
+    for (int blk = threadIdx.x; part == 1 && blk < NB; blk += 256) {
         const int kb = blk % RL;
         const int db = blk / RL;
         u32x4 r[8];
@@ -645,7 +649,8 @@ static hipError_t launch_16(const PrefillArgs& a) {
     const int n_kv_tiles = (a.Tkv + KT - 1) / KT;
     const int q_off = a.Tkv - a.Tq;
     bf16* kvt = (bf16*)a.workspace;
-    hipLaunchKernelGGL((kv_pack_kernel<DK, DV, KT>), dim3(n_kv_tiles, a.B * a.Hkv), dim3(256), 0, a.stream,
+    hipLaunchKernelGGL((kv_pack_kernel<DK, DV, KT>), dim3(n_kv_tiles, a.B * a.Hkv, 2 * DK == 1024 ? 2 : 1), dim3(256),
+                       0, a.stream,
                        (const bf16*)a.k, (const bf16*)a.v, kvt, a.Tkv, n_kv_tiles);
     const dim3 grid(n_tok_blocks, a.Hkv, a.B);
     const float sl2 = a.scale * kLog2e;
