@@ -12,8 +12,9 @@
 //     v_mfma_f32_32x32x16_bf16 with fp32 accumulation; Q stays in VGPRs,
 //     the O^T accumulator for the full value width stays in AGPRs;
 //   * online softmax per row in registers (exp2 domain, lazy rescale);
-//   * K tiles and pre-transposed V tiles are copied global->LDS with
-//     asynchronous direct-to-LDS loads, double buffered;
+//   * K tiles (from K itself, or pre-padded at d = 512) and pre-transposed
+//     V tiles are copied global->LDS with asynchronous direct-to-LDS loads,
+//     double buffered;
 //   * causal: key tiles past the block's last token are never visited, the
 //     diagonal tile is masked per element, and the heaviest blocks start
 //     first.
