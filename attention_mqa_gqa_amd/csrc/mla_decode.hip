@@ -14,7 +14,7 @@
 //     loads (non-temporal: each cached row is read once), three stages deep
 //     (two tiles in flight);
 //   * scores: wave w computes S^T = KV q_abs^T for heads 32w..32w+31 on
-//     v_mfma_f32_32x32x16_bf16 (36 contraction steps over the 576-wide
+//     v_mfma_f32_32x32x16_bf16 (or _f16; 36 contraction steps over the 576-wide
 //     row), then the online softmax of those heads;
 //   * P (bf16) of every head goes to LDS, and each wave accumulates
 //     O^T += V^T P^T for ITS quarter of the 512 value dims and all heads:
@@ -27,6 +27,7 @@
 // each workgroup stages its chunk of the index list in LDS, every copy
 // fetches the listed row (the direct-to-LDS copy takes any per-lane source
 // address), and list entries outside [0, max_len) are masked.
+// F16: fp16 queries and cache (the _f16 MFMAs, P rounded to fp16); else bf16.
 #include "common.hpp"
 #include "layout.hpp"
 #include "kernels.hpp"

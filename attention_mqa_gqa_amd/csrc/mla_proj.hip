@@ -21,6 +21,7 @@
 //     registers with byte permutes into A operands of
 //     v_mfma_f32_16x16x16_bf16 (M = value dims 8m + t, K = latent dims); the
 //     four waves split the latent and add their partial sums through LDS.
+// All three take bf16 or (F16) fp16 tensors; fp32 accumulation.
 #include "common.hpp"
 #include "kernels.hpp"
 
