@@ -385,6 +385,8 @@ MLA_SMALL = [
     (3, 128, 2000, [1, 999, 2000], "bf16"),
     (2, 16, 300, [300, 33], "f32"),
     (2, 64, 1100, [1100, 1025], "bf16"),
+    (2, 48, 500, [500, 77], "bf16"),     # heads not a multiple of 32: a wave's group is partly empty
+    (1, 112, 300, [300], "f32"),
 ]
 
 
@@ -679,6 +681,7 @@ SPARSE_SMALL = [
     (2, 64, 3000, None, 1000, "f32"),
     (2, 16, 100, [100, 1], 1, "bf16"),
     (1, 32, 40000, None, 2048, "bf16"),
+    (2, 80, 900, [900, 400], 333, "bf16"),   # 80 heads, a list length that ends inside a tile
 ]
 
 
