@@ -82,6 +82,17 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const bf16* __restrict_
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) wa[ks] = __builtin_bit_cast(bf16x8, ldg16(wrow + 16 * ks));
 
+    // RoPE part of q_abs (latent block y rotates dims 16 y .. 16 y + 15),
+    // while the weight rows are in flight
+    constexpr int kRd = kDr / (kDc / 128);
+#pragma unroll 2
+    for (int e = (int)threadIdx.x; e < B * kRd; e += 256) {
+        const int b = e / kRd, d = kRd * blockIdx.y + e % kRd;
+        const float y = rope_elem<F16>(q_rope + ((size_t)b * H + h) * kDr, d, cosv + (size_t)b * kDr,
+                                       sinv + (size_t)b * kDr);
+        q_abs[((size_t)b * H + h) * kDq + kDc + d] = st16f<F16>(y);
+    }
+
     for (int b0 = 0; b0 < B; b0 += 32) {
         const int b = b0 + n;
         const bool ok = b < B;
@@ -111,15 +122,6 @@ __global__ __launch_bounds__(256) void mla_absorb_kernel(const bf16* __restrict_
         }
     }
 
-    // RoPE part of q_abs: latent block y rotates dims 16 y .. 16 y + 15
-    constexpr int kRd = kDr / (kDc / 128);
-#pragma unroll 2
-    for (int e = (int)threadIdx.x; e < B * kRd; e += 256) {
-        const int b = e / kRd, d = kRd * blockIdx.y + e % kRd;
-        const float y = rope_elem<F16>(q_rope + ((size_t)b * H + h) * kDr, d, cosv + (size_t)b * kDr,
-                                       sinv + (size_t)b * kDr);
-        q_abs[((size_t)b * H + h) * kDq + kDc + d] = st16f<F16>(y);
-    }
 }
 
 // grid (B): row positions[b] of sequence b's cache = [c_kv | RoPE(k_pe)].
@@ -132,11 +134,15 @@ __global__ __launch_bounds__(64) void mla_cache_append_kernel(const bf16* __rest
                                                               bf16* __restrict__ kv_cache, int max_len) {
     const int b = blockIdx.x;
     const int t = threadIdx.x;
+    // every load goes out before the position is known (one memory round
+    // trip for the whole kernel)
     const int pos = positions[b];
+    const u32x4 lat = ldg16(c_kv + (size_t)b * kDc + 8 * t);             // 64 lanes x 8 = 512
+    const float rot = rope_elem<F16>(k_pe + (size_t)b * kDr, t, cosv + (size_t)b * kDr, sinv + (size_t)b * kDr);
     if (pos < 0 || pos >= max_len) return;
     bf16* row = kv_cache + ((size_t)b * max_len + pos) * kDq;
-    *(u32x4*)(row + 8 * t) = ldg16(c_kv + (size_t)b * kDc + 8 * t);      // 64 lanes x 8 = 512
-    row[kDc + t] = st16f<F16>(rope_elem<F16>(k_pe + (size_t)b * kDr, t, cosv + (size_t)b * kDr, sinv + (size_t)b * kDr));
+    *(u32x4*)(row + 8 * t) = lat;
+    row[kDc + t] = st16f<F16>(rot);
 }
 
 // grid (H, ceil(B / 16)): workgroup = one head, 16 sequences, all 128 value
