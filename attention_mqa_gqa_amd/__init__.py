@@ -171,6 +171,11 @@ def _stream_ptr(stream, device):
     return _current_raw_stream(device.index)
 
 
+def _same_dtype(what, *tensors):
+    if any(t.dtype != tensors[0].dtype for t in tensors[1:]):
+        raise TypeError(f"{what} must share a dtype")
+
+
 def _require(t, name, ndim):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
@@ -278,6 +283,7 @@ def mqa_decode(q, k_cache, v_cache, seq_lens, scale=None, out=None, out_dtype=No
     _require(k_cache, "k_cache", 4)
     _require(v_cache, "v_cache", 4)
     _require(seq_lens, "seq_lens", 1)
+    _same_dtype("q, k_cache, v_cache", q, k_cache, v_cache)
     if seq_lens.dtype != torch.int32:
         raise TypeError("seq_lens must be int32")
     B, Hq, D = q.shape
@@ -305,6 +311,7 @@ def mla_decode_absorbed(q_abs, kv_cache, seq_lens, scale=None, out=None, out_dty
     _require(q_abs, "q_abs", 3)
     _require(kv_cache, "kv_cache", 3)
     _require(seq_lens, "seq_lens", 1)
+    _same_dtype("q_abs, kv_cache", q_abs, kv_cache)
     if seq_lens.dtype != torch.int32:
         raise TypeError("seq_lens must be int32")
     B, H, DK = q_abs.shape
@@ -333,6 +340,7 @@ def mla_decode_sparse(q_abs, kv_cache, indices, scale=None, out=None, out_dtype=
     _require(q_abs, "q_abs", 3)
     _require(kv_cache, "kv_cache", 3)
     _require(indices, "indices", 2)
+    _same_dtype("q_abs, kv_cache", q_abs, kv_cache)
     if indices.dtype != torch.int32:
         raise TypeError("indices must be int32")
     B, H, DK = q_abs.shape
@@ -374,6 +382,7 @@ def mla_absorb_query(q_nope, q_rope, w_uk, cos, sin, out=None, stream=None):
     if out is None:
         out = torch.empty((B, H, 576), dtype=q_nope.dtype, device=q_nope.device)
     _require(out, "out", 3)
+    _same_dtype("q_nope, q_rope, w_uk, out", q_nope, q_rope, w_uk, out)
     st = lib.mla_absorb_query(_ptr(q_nope), _ptr(q_rope), _ptr(w_uk), _ptr(cos), _ptr(sin), _ptr(out), B, H,
                               _dtype_code(q_nope.dtype), _stream_ptr(stream, q_nope.device))
     _check(st, "mla_absorb_query")
@@ -391,6 +400,7 @@ def mla_cache_append(kv_cache, c_kv, k_pe, cos, sin, positions, stream=None):
     B, L_max, _ = kv_cache.shape
     if kv_cache.shape[2] != 576 or c_kv.shape != (B, 512) or k_pe.shape != (B, 64) or positions.shape != (B,):
         raise ValueError("kv_cache [B,L_max,576], c_kv [B,512], k_pe [B,64], positions [B]")
+    _same_dtype("kv_cache, c_kv, k_pe", kv_cache, c_kv, k_pe)
     if positions.dtype != torch.int32:
         raise TypeError("positions must be int32")
     _rope_tables(cos, sin, B, torch)
@@ -408,6 +418,7 @@ def mla_output_project(o_lat, w_uv, out=None, out_dtype=None, stream=None):
     B, H, _ = o_lat.shape
     if o_lat.shape[2] != 512 or w_uv.shape != (H, 512, 128):
         raise ValueError("o_lat [B,H,512], w_uv [H,512,128]")
+    _same_dtype("o_lat, w_uv", o_lat, w_uv)
     out_dtype = o_lat.dtype if out_dtype is None else out_dtype
     if out is None:
         out = torch.empty((B, H, 128), dtype=out_dtype, device=o_lat.device)

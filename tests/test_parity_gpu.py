@@ -291,6 +291,25 @@ def test_calls_follow_the_given_stream(torch, mqa):
     assert torch.equal(a, b)
 
 
+def test_binding_rejects_mixed_dtypes(torch, mqa):
+    """The C ABI takes one element type per call, so the binding refuses
+    16-bit tensors of different types before anything is launched."""
+    _say("binding: mixed dtypes rejected")
+    bf, hf = torch.bfloat16, torch.float16
+    z = lambda shape, dt: torch.zeros(shape, dtype=dt, device="cuda")
+    sl = torch.ones(2, dtype=torch.int32, device="cuda")
+    with pytest.raises(TypeError):
+        mqa.mqa_prefill(z((1, 16, 64, 512), bf), z((1, 1, 64, 512), hf), z((1, 1, 64, 512), bf))
+    with pytest.raises(TypeError):
+        mqa.mqa_decode(z((2, 16, 128), bf), z((2, 1, 64, 128), bf), z((2, 1, 64, 128), hf), sl)
+    with pytest.raises(TypeError):
+        mqa.mla_decode_absorbed(z((2, 16, 576), hf), z((2, 64, 576), bf), sl)
+    with pytest.raises(TypeError):
+        mqa.mla_decode_sparse(z((2, 16, 576), bf), z((2, 64, 576), hf), z((2, 8), torch.int32))
+    with pytest.raises(TypeError):
+        mqa.mla_output_project(z((2, 16, 512), bf), z((16, 512, 128), hf))
+
+
 # ---------------------------------------------------------------------------
 # decode
 # ---------------------------------------------------------------------------
