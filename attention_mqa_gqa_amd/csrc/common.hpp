@@ -163,6 +163,19 @@ __device__ __forceinline__ uint32_t pack2_t(float lo, float hi) {
     if constexpr (F16) return pack_f16x2(lo, hi);
     else return pack_bf16x2(lo, hi);
 }
+// acc + lo + hi of a packed pair of 16-bit values (one v_dot2c against
+// ones; the products are exact)
+template <bool F16>
+__device__ __forceinline__ float add_pair_t(uint32_t packed, float acc) {
+    if constexpr (F16) {
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, packed), h2{(_Float16)1.f, (_Float16)1.f}, acc, false);
+    } else {
+        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, packed), b2{(__bf16)1.f, (__bf16)1.f}, acc,
+                                               false);
+    }
+}
 template <bool F16>
 __device__ __forceinline__ bf16x8 pack8_t(const f32x4& lo, const f32x4& hi) {
     u32x4 u;

@@ -414,6 +414,12 @@ __global__ __launch_bounds__(NW * 64, (DK == 512 ? 1 : 8 / NW)) void prefill_bf1
         const char* kst = smem + ((it + 1) & 1) * KSTAGE_B;
 #pragma unroll
         for (int nt = 0; nt < NR; ++nt) sn[nt] = f32x16{};
+        // Row sums of P(t): added up next to the exponentials, except at
+        // d_qk = 128, whose phase A is the most exponential-heavy: there
+        // they are taken in phase B from the packed 16-bit probabilities
+        // (the values the MFMAs use), a pair per v_dot2c (≈1 % faster; no
+        // gain at 192, and at 512 the extra live ranges in phase B spill)
+        constexpr bool SUM_IN_B = DK == 128;
         float lsum[NR];
 #pragma unroll
         for (int nt = 0; nt < NR; ++nt) lsum[nt] = 0.f;
@@ -443,7 +449,7 @@ __global__ __launch_bounds__(NW * 64, (DK == 512 ? 1 : 8 / NW)) void prefill_bf1
                         float pr = fast_exp2(fmaf(sc[nt][i], c, -m_run[nt]));
                         asm volatile("" : "+v"(pr));
                         sc[nt][i] = pr;
-                        lsum[nt] += pr;
+                        if constexpr (!SUM_IN_B) lsum[nt] += pr;
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -452,8 +458,10 @@ __global__ __launch_bounds__(NW * 64, (DK == 512 ? 1 : 8 / NW)) void prefill_bf1
         bf16x8 pb[NR][KSP];
 #pragma unroll
         for (int nt = 0; nt < NR; ++nt) {
-            l_run[nt] += lsum[nt];
-            asm volatile("" : "+v"(l_run[nt]));
+            if constexpr (!SUM_IN_B) {
+                l_run[nt] += lsum[nt];
+                asm volatile("" : "+v"(l_run[nt]));
+            }
 #pragma unroll
             for (int kp = 0; kp < KSP; ++kp) {
                 f32x4 lo = {sc[nt][8 * kp + 0], sc[nt][8 * kp + 1], sc[nt][8 * kp + 2], sc[nt][8 * kp + 3]};
@@ -492,6 +500,14 @@ __global__ __launch_bounds__(NW * 64, (DK == 512 ? 1 : 8 / NW)) void prefill_bf1
                 const int kp = st / MT_O, mt = st % MT_O;
 #pragma unroll
                 for (int nt = 0; nt < NR; ++nt) mfma_32x32x16_acc_t<F16>(a, pb[nt][kp], o[mt][nt]);
+                if constexpr (SUM_IN_B) {
+#pragma unroll
+                    for (int wd = st * 4 * KSP / NSTEP_PV; wd < (st + 1) * 4 * KSP / NSTEP_PV; ++wd) {
+#pragma unroll
+                        for (int nt = 0; nt < NR; ++nt)
+                            l_run[nt] = add_pair_t<F16>(__builtin_bit_cast(u32x4, pb[nt][wd / 4])[wd % 4], l_run[nt]);
+                    }
+                }
                 // two scores per max3
 #pragma unroll
                 for (int i = st * 8 / NSTEP_PV; i < (st + 1) * 8 / NSTEP_PV; ++i) {
