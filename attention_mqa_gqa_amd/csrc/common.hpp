@@ -36,8 +36,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-typedef __attribute__((address_space(3))) void lds_void;
-
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // MI355X (gfx950) has 8 XCDs of 32 compute units, each XCD with its own L2;
@@ -246,18 +244,12 @@ __device__ __forceinline__ bf16x8 ldg_bf16x8_stream(const void* p) {
 }
 __device__ __forceinline__ bf16x8 ldg_bf16x8(const void* p) { return *(const bf16x8*)p; }
 
-// Asynchronous 16-byte copy global -> LDS.  Every lane supplies its own
-// global address; lane i's 16 bytes land at lds_base + 16*i (lds_base must be
-// the same for all lanes of the wave).  Completion is tracked by vmcnt.
-__device__ __forceinline__ void copy16_to_lds(const void* gptr, void* lds_base_wave) {
-    __builtin_amdgcn_global_load_lds(gptr, (lds_void*)lds_base_wave, 16, 0, 0);
-}
-
-// Same, with the source given as a wave-uniform base plus a 32-bit per-lane
-// byte offset (lets the compiler use an SGPR base and one VGPR offset).
-__device__ __forceinline__ void copy16_to_lds_off(const void* base, uint32_t byte_off, void* lds_base_wave) {
-    __builtin_amdgcn_global_load_lds((const char*)base + byte_off, (lds_void*)lds_base_wave, 16, 0, 0);
-}
+// Global -> LDS copies (global_load_lds_dwordx4: every lane supplies its own
+// global address, lane i's 16 bytes land at M0 + instruction offset + 16 i;
+// completion is tracked by vmcnt) are issued only from the inline asm below.
+// Each block writes M0 itself right before its loads, so no kernel relies on
+// M0 keeping a value across them (the compiler warns that M0 is a reserved
+// register in the clobber lists; nothing else here uses M0).
 
 // The same 16-byte global->LDS copy issued from inline asm: base (wave-
 // uniform, SGPR pair) + voff (per lane) -> LDS byte address lds_byte + 16*lane.
