@@ -624,10 +624,11 @@ def test_mla_decode_step_end_to_end(torch, mqa):
 
 
 def test_mla_step_graph_replay(torch, mqa):
-    """A whole absorbed decode step (absorb + RoPE, cache append, absorbed
-    attention with its merge, W_UV) captured once in a HIP graph through the
-    C ABI and replayed: every replay, with the program's own eager work and
-    synchronisations in between, equals the eager step bit for bit."""
+    """A whole absorbed decode step (absorb + RoPE and cache append on two
+    branches, absorbed attention with its merge, W_UV) captured once in a HIP
+    graph through the C ABI and replayed: every replay, with the program's
+    own eager work and synchronisations in between, equals the eager step
+    bit for bit."""
     _say("mla decode step as a HIP graph B6 H128 L96")
     B, H, L = 6, 128, 96
     qn, qr, ckv, kpe, wuk, wuv = (dev(torch, t) for t in mla_step_inputs(B, H, seed=24))
@@ -644,9 +645,17 @@ def test_mla_step_graph_replay(torch, mqa):
     ws = torch.empty(mqa.mla_decode_workspace_size(B, H, L), dtype=torch.uint8, device="cuda")
     cache = cache0.clone()
 
+    branch = torch.cuda.Stream()
+
     def step():
+        # absorption and cache append as two branches, joined before the
+        # attention
+        main = torch.cuda.current_stream()
+        branch.wait_stream(main)
         mqa.mla_absorb_query(qn, qr, wuk, dc, ds, out=q_abs)
-        mqa.mla_cache_append(cache, ckv, kpe, dc, ds, pos)
+        with torch.cuda.stream(branch):
+            mqa.mla_cache_append(cache, ckv, kpe, dc, ds, pos, stream=branch)
+        main.wait_stream(branch)
         mqa.mla_decode_absorbed(q_abs, cache, dsl, out=o_lat, workspace=ws)
         mqa.mla_output_project(o_lat, wuv, out=out)
 
