@@ -125,13 +125,15 @@ def _sample_rows(B, H, T, n, seed):
     return rows
 
 
-@pytest.mark.parametrize("B,Hq,Hkv,T,D", [(2, 16, 1, 4096, 512), (1, 64, 8, 8192, 128)])
-def test_prefill_bf16_full_size_sampled(torch, mqa, B, Hq, Hkv, T, D):
-    """Full-size prefill (MQA d=512 T=4096 B=2; GQA 64/8 d=128 T=8192), causal,
-    in the bench's launch configuration; sampled rows vs the oracle, plus
-    bitwise run-to-run repeatability."""
-    _say(f"prefill bf16 full B{B} Hq{Hq} Hkv{Hkv} T{T} D{D}")
-    q, k, v = prefill_inputs(B, Hq, Hkv, T, D, "bf16", seed=0)
+@pytest.mark.parametrize("B,Hq,Hkv,T,D,dt", [(2, 16, 1, 4096, 512, "bf16"), (1, 64, 8, 8192, 128, "bf16"),
+                                               (2, 16, 1, 4096, 512, "f16")])
+def test_prefill_bf16_full_size_sampled(torch, mqa, B, Hq, Hkv, T, D, dt):
+    """Full-size prefill (MQA d=512 T=4096 B=2, bf16 and fp16; GQA 64/8 d=128
+    T=8192), causal, in the bench's launch configuration; sampled rows vs the
+    oracle, plus bitwise run-to-run repeatability."""
+    _say(f"prefill {dt} full B{B} Hq{Hq} Hkv{Hkv} T{T} D{D}")
+    tol = F16_TOL if dt == "f16" else BF16_TOL
+    q, k, v = prefill_inputs(B, Hq, Hkv, T, D, dt, seed=0)
     dq, dk, dv = dev(torch, q), dev(torch, k), dev(torch, v)
     lse = torch.empty((B, Hq, T), dtype=torch.float32, device="cuda")
     out = mqa.mqa_prefill(dq, dk, dv, causal=True, lse=lse)
@@ -142,8 +144,8 @@ def test_prefill_bf16_full_size_sampled(torch, mqa, B, Hq, Hkv, T, D):
     ref, ref_lse = oracle.prefill_rows_ref(q.f32(), k.f32(), v.f32(), rows, 1 / math.sqrt(D), True)
     got = np.stack([host(out[b, h, i]) for b, h, i in rows])
     got_lse = np.array([float(lse[b, h, i]) for b, h, i in rows])
-    assert _maxerr(got, ref) <= BF16_TOL
-    assert _maxerr(got_lse, ref_lse) <= BF16_TOL
+    assert _maxerr(got, ref) <= tol
+    assert _maxerr(got_lse, ref_lse) <= tol
     assert bool(torch.isfinite(out.float()).all())
 
 
