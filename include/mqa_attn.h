@@ -22,9 +22,10 @@
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers, owned by the caller, row-major
  *     with the last dimension contiguous, and 16-byte aligned.  The library
- *     allocates nothing, keeps no state between calls, never synchronises,
- *     and enqueues its kernels on `stream` (a hipStream_t; NULL = the default
- *     stream).  Inputs are read-only; outputs and workspace are overwritten.
+ *     allocates nothing, keeps no state between calls (beyond a once-per-
+ *     process query of the device's CU count and a kernel's occupancy),
+ *     never synchronises, and enqueues its kernels on `stream` (a
+ *     hipStream_t; NULL = the default stream).  Inputs are read-only; outputs and workspace are overwritten.
  *   - Element types: MQA_DTYPE_F32 (IEEE float), MQA_DTYPE_BF16 (bfloat16)
  *     or MQA_DTYPE_F16 (IEEE half; the zdabc.icu benchmark runs its MQA
  *     operator in float16 on the GPU).  Products accumulate in fp32.
@@ -57,7 +58,7 @@ extern "C" {
 typedef enum {
     MQA_DTYPE_F32 = 0,
     MQA_DTYPE_BF16 = 1,
-    MQA_DTYPE_F16 = 2          /* IEEE half: prefill and decode only */
+    MQA_DTYPE_F16 = 2          /* IEEE half */
 } mqa_dtype;
 
 typedef enum {
