@@ -130,7 +130,20 @@ def _load():
 
 lib = _load()
 
-from torch._C import _cuda_getCurrentRawStream as _current_raw_stream  # noqa: E402
+
+def _current_raw_stream_public(index):
+    import torch
+    return torch.cuda.current_stream(index).cuda_stream
+
+
+def _pick_raw_stream_getter():
+    # torch's raw current-stream query (no Stream object per call) when this
+    # torch build has it, else the public route
+    import torch
+    return getattr(torch._C, "_cuda_getCurrentRawStream", None) or _current_raw_stream_public
+
+
+_current_raw_stream = _pick_raw_stream_getter()
 
 
 def _status_string(status):
