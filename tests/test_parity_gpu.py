@@ -164,6 +164,9 @@ PREFILL_EX_SMALL = [
     (1, 64, 8, 200, 1000, 128, 128, True, "bf16"),    # GQA chunk
     (1, 16, 2, 33, 500, 128, 128, False, "bf16"),     # no mask, T_q < T_kv
     (1, 16, 1, 64, 40, 512, 512, False, "bf16"),      # no mask, T_q > T_kv
+    # the largest group size (one token of 128 heads per workgroup)
+    (1, 128, 1, 37, 37, 512, 512, True, "bf16"),
+    (1, 128, 1, 20, 45, 192, 128, True, "bf16"),
     # multi-token decode (a few new tokens against a long cache, bottom-right
     # causal); the cache lengths end inside a key tile
     (2, 16, 1, 4, 2999, 512, 512, True, "bf16"),
