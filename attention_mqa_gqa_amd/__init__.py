@@ -198,6 +198,43 @@ def _require(t, name, ndim):
         raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
 
 
+def _require_on(t, name, device):
+    # the library reads every pointer of one call on one device
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the inputs on {device}")
+
+
+def _check_out(out, shape, device):
+    """Caller-supplied output: contiguous, on the inputs' device, exactly `shape`."""
+    _require(out, "out", len(shape))
+    _require_on(out, "out", device)
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"out must be {tuple(shape)}, got {tuple(out.shape)}")
+
+
+def _check_lse(lse, shape, device):
+    """Optional log-sum-exp output: float32, contiguous, on the device, exactly `shape`."""
+    if lse is None:
+        return
+    torch = _torch()
+    _require(lse, "lse", len(shape))
+    _require_on(lse, "lse", device)
+    if lse.dtype != torch.float32:
+        raise TypeError(f"lse must be float32, got {lse.dtype}")
+    if tuple(lse.shape) != tuple(shape):
+        raise ValueError(f"lse must be {tuple(shape)}, got {tuple(lse.shape)}")
+
+
+def _check_index(t, name, shape, device):
+    torch = _torch()
+    _require(t, name, len(shape))
+    _require_on(t, name, device)
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {tuple(shape)}, got {tuple(t.shape)}")
+
+
 def mqa_prefill_workspace_size(B, Hq, Hkv, T, head_dim, in_dtype):
     return int(lib.mqa_prefill_workspace_size(B, Hq, Hkv, T, head_dim, in_dtype))
 
@@ -219,11 +256,18 @@ def mla_decode_sparse_workspace_size(B, H, topk):
 
 
 def _workspace(nbytes, device, workspace):
+    """A caller-supplied workspace must be a contiguous tensor on `device`;
+    its size is checked by the library (MQA_ERR_WORKSPACE if too small)."""
     torch = _torch()
     if nbytes == 0:
         return None, 0
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    else:
+        if not workspace.is_cuda or workspace.device != device:
+            raise ValueError(f"workspace must be on {device}, got {workspace.device}")
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
     return workspace, workspace.numel() * workspace.element_size()
 
 
@@ -239,13 +283,14 @@ def mqa_prefill(q, k, v, causal=True, scale=None, out=None, out_dtype=None, lse=
         raise ValueError("k and v must be [B, Hkv, T, D] matching q")
     if q.dtype != k.dtype or q.dtype != v.dtype:
         raise TypeError("q, k, v must share a dtype")
+    for t, nm in ((k, "k"), (v, "v")):
+        _require_on(t, nm, q.device)
     in_code = _dtype_code(q.dtype)
     out_dtype = q.dtype if out_dtype is None else out_dtype
     if out is None:
         out = torch.empty((B, Hq, T, D), dtype=out_dtype, device=q.device)
-    _require(out, "out", 4)
-    if lse is not None:
-        _require(lse, "lse", 3)
+    _check_out(out, (B, Hq, T, D), q.device)
+    _check_lse(lse, (B, Hq, T), q.device)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     nbytes = mqa_prefill_workspace_size(B, Hq, Hkv, T, D, in_code)
     ws, wsb = _workspace(nbytes, q.device, workspace)
@@ -271,13 +316,14 @@ def mqa_prefill_ex(q, k, v, causal=True, scale=None, out=None, out_dtype=None, l
         raise ValueError("k must be [B, Hkv, T_kv, d_qk] and v [B, Hkv, T_kv, d_v]")
     if q.dtype != k.dtype or q.dtype != v.dtype:
         raise TypeError("q, k, v must share a dtype")
+    for t, nm in ((k, "k"), (v, "v")):
+        _require_on(t, nm, q.device)
     in_code = _dtype_code(q.dtype)
     out_dtype = q.dtype if out_dtype is None else out_dtype
     if out is None:
         out = torch.empty((B, Hq, T_q, DV), dtype=out_dtype, device=q.device)
-    _require(out, "out", 4)
-    if lse is not None:
-        _require(lse, "lse", 3)
+    _check_out(out, (B, Hq, T_q, DV), q.device)
+    _check_lse(lse, (B, Hq, T_q), q.device)
     scale = 1.0 / math.sqrt(DK) if scale is None else float(scale)
     nbytes = mqa_prefill_ex_workspace_size(B, Hq, Hkv, T_q, T_kv, DK, DV, in_code)
     ws, wsb = _workspace(nbytes, q.device, workspace)
@@ -295,18 +341,19 @@ def mqa_decode(q, k_cache, v_cache, seq_lens, scale=None, out=None, out_dtype=No
     _require(q, "q", 3)
     _require(k_cache, "k_cache", 4)
     _require(v_cache, "v_cache", 4)
-    _require(seq_lens, "seq_lens", 1)
     _same_dtype("q, k_cache, v_cache", q, k_cache, v_cache)
-    if seq_lens.dtype != torch.int32:
-        raise TypeError("seq_lens must be int32")
     B, Hq, D = q.shape
     Hkv, L_max = k_cache.shape[1], k_cache.shape[2]
     if k_cache.shape != (B, Hkv, L_max, D) or v_cache.shape != k_cache.shape:
         raise ValueError("caches must be [B, Hkv, L_max, D] matching q")
+    for t, nm in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _require_on(t, nm, q.device)
+    _check_index(seq_lens, "seq_lens", (B,), q.device)
     out_dtype = q.dtype if out_dtype is None else out_dtype
     if out is None:
         out = torch.empty((B, Hq, D), dtype=out_dtype, device=q.device)
-    _require(out, "out", 3)
+    _check_out(out, (B, Hq, D), q.device)
+    _check_lse(lse, (B, Hq), q.device)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     nbytes = mqa_decode_workspace_size(B, Hq, Hkv, L_max, D)
     ws, wsb = _workspace(nbytes, q.device, workspace)
@@ -323,18 +370,18 @@ def mla_decode_absorbed(q_abs, kv_cache, seq_lens, scale=None, out=None, out_dty
     torch = _torch()
     _require(q_abs, "q_abs", 3)
     _require(kv_cache, "kv_cache", 3)
-    _require(seq_lens, "seq_lens", 1)
     _same_dtype("q_abs, kv_cache", q_abs, kv_cache)
-    if seq_lens.dtype != torch.int32:
-        raise TypeError("seq_lens must be int32")
     B, H, DK = q_abs.shape
     if DK != 576 or kv_cache.shape[0] != B or kv_cache.shape[2] != 576:
         raise ValueError("q_abs must be [B,H,576] and kv_cache [B,L_max,576]")
     L_max = kv_cache.shape[1]
+    _require_on(kv_cache, "kv_cache", q_abs.device)
+    _check_index(seq_lens, "seq_lens", (B,), q_abs.device)
     out_dtype = q_abs.dtype if out_dtype is None else out_dtype
     if out is None:
         out = torch.empty((B, H, 512), dtype=out_dtype, device=q_abs.device)
-    _require(out, "out", 3)
+    _check_out(out, (B, H, 512), q_abs.device)
+    _check_lse(lse, (B, H), q_abs.device)
     scale = 1.0 / math.sqrt(192.0) if scale is None else float(scale)
     nbytes = mla_decode_workspace_size(B, H, L_max)
     ws, wsb = _workspace(nbytes, q_abs.device, workspace)
@@ -352,18 +399,18 @@ def mla_decode_sparse(q_abs, kv_cache, indices, scale=None, out=None, out_dtype=
     torch = _torch()
     _require(q_abs, "q_abs", 3)
     _require(kv_cache, "kv_cache", 3)
-    _require(indices, "indices", 2)
     _same_dtype("q_abs, kv_cache", q_abs, kv_cache)
-    if indices.dtype != torch.int32:
-        raise TypeError("indices must be int32")
     B, H, DK = q_abs.shape
-    if DK != 576 or kv_cache.shape[0] != B or kv_cache.shape[2] != 576 or indices.shape[0] != B:
+    if DK != 576 or kv_cache.shape[0] != B or kv_cache.shape[2] != 576 or indices.dim() != 2:
         raise ValueError("q_abs must be [B,H,576], kv_cache [B,L_max,576] and indices [B,topk]")
     L_max, topk = kv_cache.shape[1], indices.shape[1]
+    _require_on(kv_cache, "kv_cache", q_abs.device)
+    _check_index(indices, "indices", (B, topk), q_abs.device)
     out_dtype = q_abs.dtype if out_dtype is None else out_dtype
     if out is None:
         out = torch.empty((B, H, 512), dtype=out_dtype, device=q_abs.device)
-    _require(out, "out", 3)
+    _check_out(out, (B, H, 512), q_abs.device)
+    _check_lse(lse, (B, H), q_abs.device)
     scale = 1.0 / math.sqrt(192.0) if scale is None else float(scale)
     nbytes = mla_decode_sparse_workspace_size(B, H, topk)
     ws, wsb = _workspace(nbytes, q_abs.device, workspace)
@@ -374,9 +421,10 @@ def mla_decode_sparse(q_abs, kv_cache, indices, scale=None, out=None, out_dtype=
     return out
 
 
-def _rope_tables(cos, sin, B, torch):
+def _rope_tables(cos, sin, B, torch, device):
     for t, nm in ((cos, "cos"), (sin, "sin")):
         _require(t, nm, 2)
+        _require_on(t, nm, device)
         if t.dtype != torch.float32 or t.shape != (B, 64):
             raise ValueError(f"{nm} must be float32 [B, 64]")
 
@@ -391,10 +439,12 @@ def mla_absorb_query(q_nope, q_rope, w_uk, cos, sin, out=None, stream=None):
     B, H, _ = q_nope.shape
     if q_nope.shape[2] != 128 or q_rope.shape != (B, H, 64) or w_uk.shape != (H, 512, 128):
         raise ValueError("q_nope [B,H,128], q_rope [B,H,64], w_uk [H,512,128]")
-    _rope_tables(cos, sin, B, torch)
+    for t, nm in ((q_rope, "q_rope"), (w_uk, "w_uk")):
+        _require_on(t, nm, q_nope.device)
+    _rope_tables(cos, sin, B, torch, q_nope.device)
     if out is None:
         out = torch.empty((B, H, 576), dtype=q_nope.dtype, device=q_nope.device)
-    _require(out, "out", 3)
+    _check_out(out, (B, H, 576), q_nope.device)
     _same_dtype("q_nope, q_rope, w_uk, out", q_nope, q_rope, w_uk, out)
     st = lib.mla_absorb_query(_ptr(q_nope), _ptr(q_rope), _ptr(w_uk), _ptr(cos), _ptr(sin), _ptr(out), B, H,
                               _dtype_code(q_nope.dtype), _stream_ptr(stream, q_nope.device))
@@ -409,14 +459,14 @@ def mla_cache_append(kv_cache, c_kv, k_pe, cos, sin, positions, stream=None):
     _require(kv_cache, "kv_cache", 3)
     _require(c_kv, "c_kv", 2)
     _require(k_pe, "k_pe", 2)
-    _require(positions, "positions", 1)
     B, L_max, _ = kv_cache.shape
-    if kv_cache.shape[2] != 576 or c_kv.shape != (B, 512) or k_pe.shape != (B, 64) or positions.shape != (B,):
+    if kv_cache.shape[2] != 576 or c_kv.shape != (B, 512) or k_pe.shape != (B, 64):
         raise ValueError("kv_cache [B,L_max,576], c_kv [B,512], k_pe [B,64], positions [B]")
     _same_dtype("kv_cache, c_kv, k_pe", kv_cache, c_kv, k_pe)
-    if positions.dtype != torch.int32:
-        raise TypeError("positions must be int32")
-    _rope_tables(cos, sin, B, torch)
+    for t, nm in ((c_kv, "c_kv"), (k_pe, "k_pe")):
+        _require_on(t, nm, kv_cache.device)
+    _check_index(positions, "positions", (B,), kv_cache.device)
+    _rope_tables(cos, sin, B, torch, kv_cache.device)
     st = lib.mla_cache_append(_ptr(c_kv), _ptr(k_pe), _ptr(cos), _ptr(sin), _ptr(positions), _ptr(kv_cache), B,
                               L_max, _dtype_code(kv_cache.dtype), _stream_ptr(stream, kv_cache.device))
     _check(st, "mla_cache_append")
@@ -433,9 +483,10 @@ def mla_output_project(o_lat, w_uv, out=None, out_dtype=None, stream=None):
         raise ValueError("o_lat [B,H,512], w_uv [H,512,128]")
     _same_dtype("o_lat, w_uv", o_lat, w_uv)
     out_dtype = o_lat.dtype if out_dtype is None else out_dtype
+    _require_on(w_uv, "w_uv", o_lat.device)
     if out is None:
         out = torch.empty((B, H, 128), dtype=out_dtype, device=o_lat.device)
-    _require(out, "out", 3)
+    _check_out(out, (B, H, 128), o_lat.device)
     st = lib.mla_output_project(_ptr(o_lat), _ptr(w_uv), _ptr(out), B, H, _dtype_code(o_lat.dtype),
                                 _dtype_code(out.dtype), _stream_ptr(stream, o_lat.device))
     _check(st, "mla_output_project")
