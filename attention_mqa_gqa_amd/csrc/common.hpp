@@ -20,9 +20,6 @@
 // contraction pairs A slot j of group g with B slot j of group g.
 #pragma once
 
-#include <type_traits>
-#include <utility>
-
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -48,23 +45,6 @@ constexpr int kNumXcd = 8;
 // rare.  Exact: numerator and denominator share the same reference maximum.
 constexpr float kRescaleSlack = 8.0f;
 
-__device__ __forceinline__ f32x4 mfma_16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ f32x16 mfma_32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// The same MFMA with the accumulator pinned to AGPRs (srcC = dst = acc).
-// Used for the large O^T accumulators so that the register allocator keeps
-// them in AGPRs and the score accumulators in VGPRs.  The compiler does not
-// know this is an MFMA, so it inserts no wait states after it: every
-// accumulator is used again only several MFMAs later, and code that reads
-// the accumulators otherwise must first call mfma_acc_drain().
-__device__ __forceinline__ void mfma_32x32x16_acc(const bf16x8& a, const bf16x8& b, f32x16& acc) {
-    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
 // 24 wait states: more than any MFMA result needs before a VALU or
 // v_accvgpr_read may read it
 __device__ __forceinline__ void mfma_acc_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
@@ -85,15 +65,10 @@ __device__ __forceinline__ void scale_acc(f32x16& acc, float alpha) {
     }
 }
 
-__device__ __forceinline__ f32x4 mfma_16x16x16(const u32x2& a, const u32x2& b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
-                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
-}
-
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
-// The MFMAs above for either 16-bit element type (operands as bit containers).
+// MFMAs for either 16-bit element type (operands as bit containers).
 template <bool F16>
 __device__ __forceinline__ f32x16 mfma_32x32x16_t(const bf16x8& a, const bf16x8& b, const f32x16& c) {
     if constexpr (F16)
@@ -102,6 +77,12 @@ __device__ __forceinline__ f32x16 mfma_32x32x16_t(const bf16x8& a, const bf16x8&
     else
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+// The 32x32x16 MFMA with the accumulator pinned to AGPRs (srcC = dst =
+// acc).  Used for the large O^T accumulators so that the register allocator
+// keeps them in AGPRs and the score accumulators in VGPRs.  The compiler
+// does not know this is an MFMA, so it inserts no wait states after it:
+// every accumulator is used again only several MFMAs later, and code that
+// reads the accumulators otherwise must first call mfma_acc_drain().
 template <bool F16>
 __device__ __forceinline__ void mfma_32x32x16_acc_t(const bf16x8& a, const bf16x8& b, f32x16& acc) {
     if constexpr (F16)
@@ -127,10 +108,6 @@ __device__ __forceinline__ f32x4 mfma_16x16x16_t(const u32x2& a, const u32x2& b,
                                                          c, 0, 0, 0);
 }
 
-__device__ __forceinline__ f32x4 mfma_16x16x4_f32(float a, float b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Round-to-nearest-even fp32 -> bf16 (v_cvt_pk_bf16_f32 on gfx950).
@@ -139,15 +116,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
-}
-
-__device__ __forceinline__ bf16x8 pack_bf16x8(const f32x4& lo, const f32x4& hi) {
-    u32x4 u;
-    u.x = pack_bf16x2(lo.x, lo.y);
-    u.y = pack_bf16x2(lo.z, lo.w);
-    u.z = pack_bf16x2(hi.x, hi.y);
-    u.w = pack_bf16x2(hi.z, hi.w);
-    return __builtin_bit_cast(bf16x8, u);
 }
 
 // two floats -> two IEEE halves (round to nearest even)
@@ -183,9 +151,6 @@ __device__ __forceinline__ bf16x8 pack8_t(const f32x4& lo, const f32x4& hi) {
     u.w = pack2_t<F16>(hi.z, hi.w);
     return __builtin_bit_cast(bf16x8, u);
 }
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
 // Byte permute: bytes 0-3 come from `lo`, 4-7 from `hi`.
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
@@ -246,60 +211,43 @@ __device__ __forceinline__ bf16x8 ldg_bf16x8(const void* p) { return *(const bf1
 
 // Global -> LDS copies (global_load_lds_dwordx4: every lane supplies its own
 // global address, lane i's 16 bytes land at M0 + instruction offset + 16 i;
-// completion is tracked by vmcnt) are issued only from the inline asm below.
-// Each block writes M0 itself right before its loads, so no kernel relies on
-// M0 keeping a value across them (the compiler warns that M0 is a reserved
-// register in the clobber lists; nothing else here uses M0).
+// completion is tracked by vmcnt) are issued only from the inline asm below,
+// which takes the LDS byte address as an operand constrained to M0: the
+// compiler writes M0 itself and knows it is live, so no value it keeps in
+// M0 is lost across these blocks.
+// Inline asm (not the builtin) because the compiler stops tracking LDS
+// reads precisely while it sees an LDS DMA in flight and waits for all of
+// them (lgkmcnt(0)) before every use.  The asm has no register outputs;
+// callers wait with wait_vmcnt<0>() and a barrier before reading the
+// destination.  The leading s_nop covers a VALU->SGPR->VMEM read hazard on
+// the base and the M0 write right before the copy.
 
-// The same 16-byte global->LDS copy issued from inline asm: base (wave-
-// uniform, SGPR pair) + voff (per lane) -> LDS byte address lds_byte + 16*lane.
-// Used inside loops that also read LDS: when the compiler sees an LDS DMA in
-// flight it stops tracking LDS reads precisely and waits for all of them
-// (lgkmcnt(0)) before every use.  The asm has no register outputs; callers
-// wait with wait_vmcnt<0>() and a barrier before reading the destination.
-// The leading s_nop covers a VALU->SGPR->VMEM read hazard on the base.
+// base (wave-uniform, SGPR pair) + voff (per lane) -> LDS byte address
+// lds_byte + 16*lane.
 __device__ __forceinline__ void copy16_to_lds_async(const void* base, uint32_t voff, uint32_t lds_byte) {
     asm volatile(
         "s_nop 4\n\t"
-        "s_mov_b32 m0, %2\n\t"
         "global_load_lds_dwordx4 %0, %1"
         :
-        : "v"(voff), "s"(base), "s"(lds_byte)
-        : "memory", "m0");
+        : "v"(voff), "s"(base), "{m0}"(lds_byte)
+        : "memory");
 }
 
 // Four 1 KB copies S bytes apart (global base + S k -> LDS lds_byte + S k,
-// k = 0..3) under one M0 write: the instruction offset moves both the
+// k = 0..3) under one M0 value: the instruction offset moves both the
 // global and the LDS address.
 template <int S>
 __device__ __forceinline__ void copy4_to_lds_async(const void* base, uint32_t voff, uint32_t lds_byte) {
     static_assert(S >= 1024 && 3 * S < 4096, "offset field");
     asm volatile(
         "s_nop 4\n\t"
-        "s_mov_b32 m0, %2\n\t"
         "global_load_lds_dwordx4 %0, %1\n\t"
         "global_load_lds_dwordx4 %0, %1 offset:%3\n\t"
         "global_load_lds_dwordx4 %0, %1 offset:%4\n\t"
         "global_load_lds_dwordx4 %0, %1 offset:%5"
         :
-        : "v"(voff), "s"(base), "s"(lds_byte), "n"(S), "n"(2 * S), "n"(3 * S)
-        : "memory", "m0");
-}
-
-// Four consecutive 1 KB copies (global base + 1024 k -> LDS lds_byte +
-// 1024 k, k = 0..3) under one M0 write: the instruction offset moves both
-// the global and the LDS address.
-__device__ __forceinline__ void copy4x1k_to_lds_async(const void* base, uint32_t voff, uint32_t lds_byte) {
-    asm volatile(
-        "s_nop 4\n\t"
-        "s_mov_b32 m0, %2\n\t"
-        "global_load_lds_dwordx4 %0, %1\n\t"
-        "global_load_lds_dwordx4 %0, %1 offset:1024\n\t"
-        "global_load_lds_dwordx4 %0, %1 offset:2048\n\t"
-        "global_load_lds_dwordx4 %0, %1 offset:3072"
-        :
-        : "v"(voff), "s"(base), "s"(lds_byte)
-        : "memory", "m0");
+        : "v"(voff), "s"(base), "{m0}"(lds_byte), "n"(S), "n"(2 * S), "n"(3 * S)
+        : "memory");
 }
 
 // The same copy with the non-temporal hint, for data read exactly once
@@ -307,25 +255,10 @@ __device__ __forceinline__ void copy4x1k_to_lds_async(const void* base, uint32_t
 __device__ __forceinline__ void copy16_to_lds_async_stream(const void* base, uint32_t voff, uint32_t lds_byte) {
     asm volatile(
         "s_nop 4\n\t"
-        "s_mov_b32 m0, %2\n\t"
         "global_load_lds_dwordx4 %0, %1 nt"
         :
-        : "v"(voff), "s"(base), "s"(lds_byte)
-        : "memory", "m0");
-}
-
-// Same, with up to VALU vector-ALU instructions (transcendentals included)
-// placed after each MFMA: lets independent softmax work fill the MFMA
-// shadow of a single wave.
-template <int FIRST, int STEPS, int VALU>
-__device__ __forceinline__ void sched_reads_ahead_valu() {
-    __builtin_amdgcn_sched_group_barrier(0x100, FIRST, 0);
-#pragma unroll
-    for (int i = 0; i < STEPS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x402, VALU, 0);
-    }
+        : "v"(voff), "s"(base), "{m0}"(lds_byte)
+        : "memory");
 }
 
 template <int N>
@@ -362,16 +295,6 @@ __device__ __forceinline__ void sched_reads_ahead() {
     }
 }
 
-
-// Compile-time loop: f(std::integral_constant<int, 0>{}) ... up to N - 1.
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
-    (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-    static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }

@@ -283,7 +283,7 @@ __global__ __launch_bounds__(NW * 64, (DK == 512 ? 1 : 8 / NW)) void prefill_bf1
         const char* src = KVbh + (size_t)tile * TILE_B + KSTREAM_B;
         const uint32_t dst = lds_base + (uint32_t)(2 * KSTAGE_B + (tile & 1) * VSTAGE_B);
         const int inst = (g * NW + w) * 4;
-        copy4x1k_to_lds_async(src + inst * 1024, lane16, dst + (uint32_t)inst * 1024u);
+        copy4_to_lds_async<1024>(src + inst * 1024, lane16, dst + (uint32_t)inst * 1024u);
     };
     auto issue_v = [&](int tile) {
         const char* src = KVbh + (size_t)tile * TILE_B + KSTREAM_B;

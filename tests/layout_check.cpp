@@ -9,76 +9,7 @@ using namespace mqa::layout;
 static int fail(const char* what, int a, int b) { std::printf("FAIL %s (%d, %d)\n", what, a, b); return 1; }
 
 int main() {
-    // 1. Each 32-key step: S^T rows of the two M-tiles cover keys 0..31 once,
-    //    and accumulator (mt, g, i) agrees with row 4g+i of M-tile mt.
-    for (int a = 0; a < 2; ++a) {
-        std::set<int> keys;
-        for (int h = 0; h < 2; ++h)
-            for (int m = 0; m < 16; ++m) keys.insert(st_row_key(2 * a + h, m));
-        if ((int)keys.size() != 32 || *keys.begin() != 32 * a || *keys.rbegin() != 32 * a + 31) return fail("st rows", a, 0);
-        for (int mt = 2 * a; mt < 2 * a + 2; ++mt)
-            for (int g = 0; g < 4; ++g)
-                for (int i = 0; i < 4; ++i)
-                    if (st_c_key(mt, g, i) != st_row_key(mt, 4 * g + i)) return fail("st c/row", mt, g);
-        // lane group g holds keys 8g..8g+7 of the step: the P.V contraction slots
-        for (int g = 0; g < 4; ++g)
-            for (int j = 0; j < 8; ++j)
-                if (st_c_key(2 * a + (j >> 2), g, j & 3) != 32 * a + 8 * g + j) return fail("pv slots", g, j);
-    }
-    // 2. Swizzles are bijections within a row.
-    for (int r = 0; r < 64; ++r) {
-        std::set<int> s16, s8, s4;
-        for (int c = 0; c < 64; ++c) s16.insert(c ^ kswz(r));
-        for (int c = 0; c < 8; ++c) s8.insert(c ^ swz8(r));
-        for (int c = 0; c < 4; ++c) s4.insert(c ^ swz4(r));
-        if (s16.size() != 64 || *s16.rbegin() != 63 || s8.size() != 8 || *s8.rbegin() != 7 || s4.size() != 4 || *s4.rbegin() != 3)
-            return fail("bijection", r, 0);
-    }
-    // 3. Bank slots (16-byte units mod 256 bytes) are distinct over the 16
-    //    lanes of one lane group for every operand read.
-    for (int rowbytes : {256, 1024, 1152 - 128}) {   // K tile rows (D = 128, 512; MLA latent 512)
-        for (int mt = 0; mt < 4; ++mt)
-            for (int ks = 0; ks < rowbytes / 64; ++ks)
-                for (int g = 0; g < 4; ++g) {
-                    std::set<int> slots;
-                    for (int m = 0; m < 16; ++m) {
-                        int kk = st_row_key(mt, m);
-                        int pos = (4 * ks + g) ^ kswz(kk);
-                        long addr = (long)kk * rowbytes + pos * 16;
-                        slots.insert((int)((addr / 16) % 16));
-                    }
-                    if (slots.size() != 16) return fail("K reads", rowbytes, ks);
-                }
-    }
-    for (int mt = 0; mt < 4; ++mt)       // 128-byte rows (MLA RoPE part)
-        for (int g = 0; g < 4; ++g)
-            for (int ks = 0; ks < 2; ++ks) {
-                std::set<int> slots;
-                for (int m = 0; m < 16; ++m) {
-                    int kk = st_row_key(mt, m);
-                    long addr = (long)kk * 128 + (((4 * ks + g) ^ swz8(kk)) * 16);
-                    slots.insert((int)((addr / 16) % 16));
-                }
-                if (slots.size() != 16) return fail("rope reads", mt, g);
-            }
-    for (int rl : {4, 8})                 // V^T rows of rl chunks
-        for (int mt = 0; mt < 32; ++mt)
-            for (int kp = 0; kp < rl / 4; ++kp)
-                for (int g = 0; g < 4; ++g) {
-                    std::set<int> slots;
-                    for (int m = 0; m < 16; ++m) {
-                        int d = pv_row_d(mt, m);
-                        long addr = ((long)d * rl + ((4 * kp + g) ^ vswz(d, rl))) * 16;
-                        slots.insert((int)((addr / 16) % 16));
-                    }
-                    if (slots.size() != 16) return fail("V reads", rl, mt);
-                }
-    // 4. Output columns: accumulators (2b, g, 0..3) and (2b+1, g, 0..3) are 8 consecutive dims.
-    for (int b = 0; b < 16; ++b)
-        for (int g = 0; g < 4; ++g)
-            for (int j = 0; j < 8; ++j)
-                if (pv_c_d(2 * b + (j >> 2), g, j & 3) != 32 * b + 8 * g + j) return fail("out cols", b, g);
-    // 5. 32x32x16 maps: accumulator (h, i) is row 8(i/4)+4h+i%4 of the A operand,
+    // 1. 32x32x16 maps: accumulator (h, i) is row 8(i/4)+4h+i%4 of the A operand,
     //    i.e. key swap23(row); the two lane halves cover each 16-key step.
     for (int h = 0; h < 2; ++h)
         for (int i = 0; i < 16; ++i)
@@ -89,7 +20,7 @@ int main() {
             for (int j = 0; j < 8; ++j) keys.insert(c32_index(h, 8 * ks + j));
         if ((int)keys.size() != 16 || *keys.begin() != 16 * ks) return fail("c32 kstep", ks, 0);
     }
-    // 6. 32-row operand reads: 8-lane groups hit 8 distinct slots of 128 B and
+    // 2. 32-row operand reads: 8-lane groups hit 8 distinct slots of 128 B and
     //    16-lane groups 16 distinct slots of 256 B.
     auto grp_ok = [](auto addr) {
         for (int grp : {8, 16}) {
@@ -121,7 +52,7 @@ int main() {
                 if ((c ^ swz32(r, rc)) / gs != c / gs) return fail("swz32 group", rc, r);
         }
     }
-    // 7. Padded 1 KB rows: lane l reads row position l % 32 (key
+    // 3. Padded 1 KB rows: lane l reads row position l % 32 (key
     //    swap23(l % 32)), chunk 2 ks + l / 32.
     for (int ks = 0; ks < 32; ++ks) {
         auto addr = [&](int l) { return (long)(l % 32) * padded_row_bytes(1024) + (2 * ks + l / 32) * 16; };
@@ -129,7 +60,7 @@ int main() {
     }
     for (int r = 0; r < 64; ++r)
         if (padded_row_pos(padded_row_pos(r)) != r || padded_row_pos(r) / 32 != r / 32) return fail("padded pos", r, 0);
-    // 8. MLA tiles: latent score reads (lane l: row l % 32, chunk 2 ks + l / 32),
+    // 4. MLA tiles: latent score reads (lane l: row l % 32, chunk 2 ks + l / 32),
     //    RoPE reads, P^T operand reads (row = head 32 nt + l % 32) and the
     //    transposing 64-bit V^T reads (16-lane groups: 4 rows x 32 bytes).
     {
