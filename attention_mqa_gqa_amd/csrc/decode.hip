@@ -321,21 +321,24 @@ hipError_t merge_launch(const float* part_o, const float* part_ml, const int32_t
 // splits: each workgroup pays a load latency before its first step and a
 // partial write), never under min_chunk rows.
 // ---------------------------------------------------------------------------
-static int round_up(int x, int m) { return (x + m - 1) / m * m; }
+// 64-bit throughout: the planners also answer workspace queries for sizes
+// the launch itself would reject.
+static long long round_up(long long x, long long m) { return (x + m - 1) / m * m; }
 
 DecodePlan decode_plan(int B, int Hkv, int max_len, int head_dim) {
-    const long units = (long)B * Hkv;
-    const int step = head_dim == 512 ? 4 * 16 : 4 * 64;      // NW * STEP
-    const int min_chunk = head_dim == 512 ? 2048 : 1024;
-    const long target_wgs = 1024;
-    long want = ((long)max_len * units + target_wgs - 1) / target_wgs;
-    int chunk = (int)(want > max_len ? max_len : want);
+    const long long units = (long long)B * Hkv;
+    const long long step = head_dim == 512 ? 4 * 16 : 4 * 64;      // NW * STEP
+    const long long min_chunk = head_dim == 512 ? 2048 : 1024;
+    const long long target_wgs = 1024;
+    const long long want = ((long long)max_len * units + target_wgs - 1) / target_wgs;
+    long long chunk = want > max_len ? (long long)max_len : want;
     if (chunk < min_chunk) chunk = min_chunk;
     chunk = round_up(chunk, step);
+    long long n_split = ((long long)max_len + chunk - 1) / chunk;
+    if (n_split < 1) n_split = 1;
     DecodePlan p;
-    p.chunk = chunk;
-    p.n_split = (max_len + chunk - 1) / chunk;
-    if (p.n_split < 1) p.n_split = 1;
+    p.chunk = (int)(chunk > 0x7FFFFFC0LL ? 0x7FFFFFC0LL : chunk);
+    p.n_split = (int)n_split;
     return p;
 }
 

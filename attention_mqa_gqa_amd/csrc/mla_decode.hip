@@ -437,32 +437,36 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
     }
 }
 
+// 64-bit arithmetic: the planners also answer workspace queries for sizes
+// the launch itself would reject.
 DecodePlan mla_plan(int B, int max_len) {
     // one workgroup per CU (LDS-bound): about 256 workgroups in total
-    const int target_wgs = 256;
-    int splits = (target_wgs + B - 1) / B;
-    int chunk = (max_len + splits - 1) / splits;
+    const long long target_wgs = 256;
+    const long long splits = (target_wgs + B - 1) / B;
+    long long chunk = ((long long)max_len + splits - 1) / splits;
     if (chunk < 512) chunk = 512;
     chunk = (chunk + kKT - 1) / kKT * kKT;
+    long long n_split = ((long long)max_len + chunk - 1) / chunk;
+    if (n_split < 1) n_split = 1;
     DecodePlan p;
-    p.chunk = chunk;
-    p.n_split = (max_len + chunk - 1) / chunk;
-    if (p.n_split < 1) p.n_split = 1;
+    p.chunk = (int)chunk;
+    p.n_split = (int)n_split;
     return p;
 }
 
 DecodePlan mla_sparse_plan(int B, int topk) {
     // about 256 workgroups; 128 .. kMaxSparseChunk list entries each
-    const int target_wgs = 256;
-    int splits = (target_wgs + B - 1) / B;
-    int chunk = (topk + splits - 1) / splits;
+    const long long target_wgs = 256;
+    const long long splits = (target_wgs + B - 1) / B;
+    long long chunk = ((long long)topk + splits - 1) / splits;
     if (chunk < 128) chunk = 128;
     chunk = (chunk + kKT - 1) / kKT * kKT;
     if (chunk > kMaxSparseChunk) chunk = kMaxSparseChunk;
+    long long n_split = ((long long)topk + chunk - 1) / chunk;
+    if (n_split < 1) n_split = 1;
     DecodePlan p;
-    p.chunk = chunk;
-    p.n_split = (topk + chunk - 1) / chunk;
-    if (p.n_split < 1) p.n_split = 1;
+    p.chunk = (int)chunk;
+    p.n_split = (int)n_split;
     return p;
 }
 

@@ -236,3 +236,50 @@ def test_decode_workspace_grows_with_splits():
     assert b >= a > 0
     # partials: (D + 2) floats per (sequence, head, split)
     assert a % (64 * 16 * (512 + 2) * 4) == 0
+
+
+def _gpu_present():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_gpu_present(), reason="forces a launch failure: only on a host without a GPU")
+def test_launch_failure_is_reported_as_hip_error():
+    """Valid arguments on a host with no GPU: validation passes, the kernel
+    launch fails in the HIP runtime, and the call returns MQA_ERR_HIP with
+    the runtime's error name (the library never aborts).  A later call that
+    fails validation returns its own status and leaves the HIP error name as
+    it was."""
+    need = lib.mqa_prefill_workspace_size(1, 16, 1, 128, 512, BF16)
+    assert _prefill(wsb=need) == -4
+    assert lib.mqa_last_hip_error_name() not in (b"hipSuccess", b"")
+    dws = lib.mqa_decode_workspace_size(2, 16, 1, 64, 512)
+    assert lib.mqa_decode(P, P, P, P, P, None, 2, 16, 1, 64, 512, 0.05, BF16, BF16, P, dws, None) == -4
+    mws = lib.mla_decode_workspace_size(2, 16, 64)
+    assert lib.mla_decode_absorbed(P, P, P, P, None, 2, 16, 64, 0.07, BF16, BF16, P, mws, None) == -4
+    name = lib.mqa_last_hip_error_name()
+    assert _prefill(Hkv=3) == INVALID
+    assert lib.mqa_last_hip_error_name() == name
+
+
+PEAKS_HEADER = os.path.join(ROOT, "include", "mqa_peaks.h")
+
+
+def test_peaks_header_functions_are_exported():
+    """libmqa_peaks.so (the attainable-peak probes) exports what its header
+    declares, and rejects bad arguments before any launch."""
+    from attention_mqa_gqa_amd import peaks
+    text = re.sub(r"/\*.*?\*/", "", open(PEAKS_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\**\s+\**([a-z_0-9]+)\s*\(", text, flags=re.M)))
+    assert names == sorted(peaks.EXPORTED_SYMBOLS)
+    pl = peaks.load()
+    for n in names:
+        assert hasattr(pl, n), n
+    assert pl.mqa_peak_mfma_bf16(3, 10, P, P, None) == -1
+    assert pl.mqa_peak_mfma_bf16(1, 0, P, P, None) == -1
+    assert pl.mqa_peak_hbm_read(MIS, 1 << 20, P, None) == -1
+    assert pl.mqa_peak_hbm_copy(P, MIS, 1 << 20, None) == -1
+    assert pl.mqa_peak_lds_read(17, 10, P, None) == -1
