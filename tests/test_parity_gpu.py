@@ -5,7 +5,7 @@ bf16-rounded values the device gets, upcast exactly.  Bars: max |err| <=
 2e-2 for bf16 inputs, <= 1e-5 for fp32 (both on outputs and on the
 natural-log LSE).  Small cases are compared element by element; the
 full-size workloads (in the launch configuration the bench times) are
-compared on sampled rows / sequences that the oracle recomputes one by one.
+compared element by element in test_parity_full_gpu.py.
 """
 
 import math
@@ -90,6 +90,11 @@ PREFILL_SMALL = [
     (1, 12, 4, 65, 128, False, "bf16"),
     (1, 12, 1, 99, 512, True, "bf16"),        # group of 12 (not a power of two): 10 tokens per block
     (2, 6, 1, 70, 128, True, "f32"),          # group of 6
+    # d = 128 groups above 128 heads (up to the 256 rows of a workgroup):
+    # one token of all 256 heads per workgroup; 200 heads (1 token, 56 idle rows)
+    (1, 256, 1, 37, 128, True, "bf16"),
+    (1, 200, 1, 45, 128, True, "f32"),
+    (2, 512, 2, 19, 128, False, "bf16"),
 ]
 
 
@@ -118,35 +123,19 @@ def test_prefill_f32_ragged_and_gqa(torch, mqa):
         assert _maxerr(host(out), ref) <= F32_TOL
 
 
-def _sample_rows(B, H, T, n, seed):
-    rng = np.random.default_rng(seed)
-    rows = [(0, 0, 0), (B - 1, H - 1, T - 1), (0, H - 1, T - 1), (B - 1, 0, 1)]
-    rows += [(int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(T))) for _ in range(n)]
-    return rows
-
-
-@pytest.mark.parametrize("B,Hq,Hkv,T,D,dt", [(2, 16, 1, 4096, 512, "bf16"), (1, 64, 8, 8192, 128, "bf16"),
-                                               (2, 16, 1, 4096, 512, "f16")])
-def test_prefill_bf16_full_size_sampled(torch, mqa, B, Hq, Hkv, T, D, dt):
-    """Full-size prefill (MQA d=512 T=4096 B=2, bf16 and fp16; GQA 64/8 d=128
-    T=8192), causal, in the bench's launch configuration; sampled rows vs the
-    oracle, plus bitwise run-to-run repeatability."""
-    _say(f"prefill {dt} full B{B} Hq{Hq} Hkv{Hkv} T{T} D{D}")
-    tol = F16_TOL if dt == "f16" else BF16_TOL
-    q, k, v = prefill_inputs(B, Hq, Hkv, T, D, dt, seed=0)
-    dq, dk, dv = dev(torch, q), dev(torch, k), dev(torch, v)
-    lse = torch.empty((B, Hq, T), dtype=torch.float32, device="cuda")
-    out = mqa.mqa_prefill(dq, dk, dv, causal=True, lse=lse)
-    out2 = mqa.mqa_prefill(dq, dk, dv, causal=True)
-    torch.cuda.synchronize()
-    assert torch.equal(out, out2)
-    rows = _sample_rows(B, Hq, T, 40, seed=5)
-    ref, ref_lse = oracle.prefill_rows_ref(q.f32(), k.f32(), v.f32(), rows, 1 / math.sqrt(D), True)
-    got = np.stack([host(out[b, h, i]) for b, h, i in rows])
-    got_lse = np.array([float(lse[b, h, i]) for b, h, i in rows])
-    assert _maxerr(got, ref) <= tol
-    assert _maxerr(got_lse, ref_lse) <= tol
-    assert bool(torch.isfinite(out.float()).all())
+@pytest.mark.parametrize("D", [64, 192, 256, 320, 384, 448])
+def test_prefill_f32_every_width(torch, mqa, D):
+    """fp32 prefill at every width the fp32 kernel is built for (64 .. 512 in
+    steps of 64; 128 and 512 are covered above), causal and full, GQA."""
+    _say(f"prefill f32 B2 Hq6 Hkv2 T45 D{D}")
+    q, k, v = prefill_inputs(2, 6, 2, 45, D, "f32", seed=30 + D)
+    for causal in (True, False):
+        lse = torch.empty((2, 6, 45), dtype=torch.float32, device="cuda")
+        out = mqa.mqa_prefill(dev(torch, q), dev(torch, k), dev(torch, v), causal=causal, lse=lse)
+        torch.cuda.synchronize()
+        ref, ref_lse = oracle.prefill_ref(q.f32(), k.f32(), v.f32(), 1 / math.sqrt(D), causal)
+        assert _maxerr(host(out), ref) <= F32_TOL
+        assert _maxerr(host(lse), ref_lse) <= F32_TOL
 
 
 # ---------------------------------------------------------------------------
@@ -247,30 +236,6 @@ def test_prefill_ex_square_matches_prefill(torch, mqa):
     assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("B,Hq,Hkv,Tq,Tkv,DK,DV", [(1, 128, 128, 8192, 8192, 192, 128),
-                                                  (2, 16, 1, 1024, 8192, 512, 512)])
-def test_prefill_ex_full_size_sampled(torch, mqa, B, Hq, Hkv, Tq, Tkv, DK, DV):
-    """Full-size expanded MLA prefill (H=128, d 192/128, T=8192) and MQA
-    chunked prefill (1024 new tokens after 7168, d=512), causal, in the
-    bench's launch configuration: sampled rows vs the oracle and bitwise
-    run-to-run repeatability."""
-    _say(f"prefill_ex bf16 full B{B} Hq{Hq} Hkv{Hkv} Tq{Tq} Tkv{Tkv} DK{DK} DV{DV}")
-    q, k, v = prefill_inputs(B, Hq, Hkv, Tq, DK, "bf16", seed=0, d_v=DV, T_kv=Tkv)
-    dq, dk, dv = dev(torch, q), dev(torch, k), dev(torch, v)
-    lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device="cuda")
-    out = mqa.mqa_prefill_ex(dq, dk, dv, causal=True, lse=lse)
-    out2 = mqa.mqa_prefill_ex(dq, dk, dv, causal=True)
-    torch.cuda.synchronize()
-    assert torch.equal(out, out2)
-    rows = _sample_rows(B, Hq, Tq, 40, seed=6)
-    ref, ref_lse = oracle.prefill_rows_ref(q.f32(), k.f32(), v.f32(), rows, 1 / math.sqrt(DK), True)
-    got = np.stack([host(out[b, h, i]) for b, h, i in rows])
-    got_lse = np.array([float(lse[b, h, i]) for b, h, i in rows])
-    assert _maxerr(got, ref) <= BF16_TOL
-    assert _maxerr(got_lse, ref_lse) <= BF16_TOL
-    assert bool(torch.isfinite(out.float()).all())
-
-
 def test_calls_follow_the_given_stream(torch, mqa):
     """The library enqueues on the stream it is given: work queued on a side
     stream behind a long kernel still reads the inputs as they are when it
@@ -331,6 +296,11 @@ DECODE_SMALL = [
     # first (B <= 256), and in index order above that
     (160, 16, 8, 600, 128, (1, 600), "bf16"),
     (300, 8, 8, 64, 128, (1, 64), "f32"),
+    # d = 128 with 12 and 16 query heads per KV head (12 of the 16 MFMA
+    # columns used; all 16)
+    (3, 24, 2, 1500, 128, [1500, 17, 1024], "bf16"),
+    (2, 16, 1, 2100, 128, [2100, 999], "f32"),
+    (2, 32, 2, 700, 128, [1, 700], "bf16"),
 ]
 
 
@@ -364,40 +334,6 @@ def test_decode_zero_length_and_repeatability(torch, mqa):
     ref, _ = oracle.decode_ref(q.f32()[[0, 2]], kc.f32()[[0, 2]], vc.f32()[[0, 2]], np.array([4500, 2500]),
                                1 / math.sqrt(512))
     assert _maxerr(host(out[[0, 2]]), ref) <= BF16_TOL
-
-
-def _decode_full_check(torch, mqa, B, Hq, Hkv, L, D, lengths, samples):
-    q, kc, vc, sl = decode_inputs(B, Hq, Hkv, L, D, "bf16", seed=0, lengths=lengths)
-    dq, dk, dv = dev(torch, q), dev(torch, kc), dev(torch, vc)
-    del kc, vc
-    dsl = torch.from_numpy(sl).cuda()
-    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
-    out = mqa.mqa_decode(dq, dk, dv, dsl, lse=lse)
-    out2 = mqa.mqa_decode(dq, dk, dv, dsl)
-    torch.cuda.synchronize()
-    assert torch.equal(out, out2)
-    assert bool(torch.isfinite(out.float()).all())
-    for b in samples:
-        Lb = int(sl[b])
-        qs, ks, vs = decode_slice(0, b, Hq, Hkv, Lb, D)
-        ref, ref_lse = oracle.decode_ref(round_bf16(qs)[None], round_bf16(ks)[None], round_bf16(vs)[None],
-                                         np.array([Lb]), 1 / math.sqrt(D))
-        assert _maxerr(host(out[b]), ref[0]) <= BF16_TOL
-        assert _maxerr(host(lse[b]), ref_lse[0]) <= BF16_TOL
-
-
-def test_decode_full_size_mqa(torch, mqa):
-    """MQA decode batch 64, Hq=16, Hkv=1, d=512, cache 8192 (bench configuration)."""
-    _say("decode full B64 Hq16 Hkv1 L8192 D512")
-    _decode_full_check(torch, mqa, 64, 16, 1, 8192, 512, None, samples=[0, 17, 63])
-
-
-def test_decode_full_size_gqa(torch, mqa):
-    """GQA decode batch 128, Hq=64, Hkv=8, d=128, lengths U[1024, 16384]."""
-    _say("decode full B128 Hq64 Hkv8 L16384 D128 lengths U[1024,16384]")
-    sl = draw_lengths(128, (1024, 16384), 16384, 0)
-    samples = [0, int(np.argmin(sl)), int(np.argmax(sl)), 127]
-    _decode_full_check(torch, mqa, 128, 64, 8, 16384, 128, (1024, 16384), samples)
 
 
 # ---------------------------------------------------------------------------
@@ -462,27 +398,6 @@ def test_mla_f16(torch, mqa, B, H, L, lengths, topk, odt):
     _say(f"  max |err| {err:.2e}")
     assert err <= F16_TOL
     assert _maxerr(host(lse), ref_lse) <= F16_TOL
-
-
-def test_mla_full_size(torch, mqa):
-    """MLA absorbed decode batch 32, H=128, context 32768, scale 1/sqrt(192)."""
-    _say("mla full B32 H128 L32768")
-    B, H, L = 32, 128, 32768
-    q, kv, sl = mla_inputs(B, H, L, 576, "bf16", seed=0)
-    dq, dkv = dev(torch, q), dev(torch, kv)
-    del kv
-    dsl = torch.from_numpy(sl).cuda()
-    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
-    out = mqa.mla_decode_absorbed(dq, dkv, dsl, lse=lse)
-    out2 = mqa.mla_decode_absorbed(dq, dkv, dsl)
-    torch.cuda.synchronize()
-    assert torch.equal(out, out2)
-    scale = 1 / math.sqrt(192)
-    for b in (0, 31):
-        qs, kvs = mla_slice(0, b, H, L)
-        ref, ref_lse = oracle.mla_absorbed_ref(round_bf16(qs)[None], round_bf16(kvs)[None], np.array([L]), scale)
-        assert _maxerr(host(out[b]), ref[0]) <= BF16_TOL
-        assert _maxerr(host(lse[b]), ref_lse[0]) <= BF16_TOL
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,L,D,lengths,odt", [(4, 16, 1, 3000, 512, (1, 3000), "f16"),
@@ -754,29 +669,6 @@ def test_mla_sparse_all_rows_equals_dense(torch, mqa):
     de = mqa.mla_decode_absorbed(dev(torch, q), dev(torch, kv), torch.from_numpy(sl).cuda())
     torch.cuda.synchronize()
     assert _maxerr(host(sp), host(de)) <= BF16_TOL
-
-
-def test_mla_sparse_full_size(torch, mqa):
-    """Sparse MLA decode batch 32, H=128, cache 32768, 2048 selected rows per
-    sequence (the bench configuration); sampled sequences vs the oracle and
-    bitwise run-to-run repeatability."""
-    _say("mla sparse full B32 H128 L32768 topk 2048")
-    B, H, L, k = 32, 128, 32768, 2048
-    q, kv, sl = mla_inputs(B, H, L, 576, "bf16", seed=0)
-    idx = draw_topk(B, sl, k, seed=0)
-    dq, dkv, didx = dev(torch, q), dev(torch, kv), torch.from_numpy(idx).cuda()
-    del kv
-    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
-    out = mqa.mla_decode_sparse(dq, dkv, didx, lse=lse)
-    out2 = mqa.mla_decode_sparse(dq, dkv, didx)
-    torch.cuda.synchronize()
-    assert torch.equal(out, out2)
-    scale = 1 / math.sqrt(192)
-    for b in (0, 13, 31):
-        qs, kvs = mla_slice(0, b, H, L)
-        ref, ref_lse = oracle.mla_sparse_ref(round_bf16(qs)[None], round_bf16(kvs)[None], idx[b:b + 1], scale)
-        assert _maxerr(host(out[b]), ref[0]) <= BF16_TOL
-        assert _maxerr(host(lse[b]), ref_lse[0]) <= BF16_TOL
 
 
 # ---------------------------------------------------------------------------
