@@ -1,8 +1,10 @@
-"""Build libmqa_attn.so in-tree with hipcc for gfx950.
+"""Build libmqa_attn.so (and the probe library libmqa_peaks.so) in-tree
+with hipcc for gfx950.
 
 ``python attention_mqa_gqa_amd/build.py`` (or ``build_library()``) compiles
 every ``csrc/*.hip`` file to an object and links them into
-``attention_mqa_gqa_amd/libmqa_attn.so``.  It always recompiles.
+``attention_mqa_gqa_amd/libmqa_attn.so``, and ``peaks/peaks.hip`` into
+``attention_mqa_gqa_amd/libmqa_peaks.so``.  It always recompiles.
 """
 
 from __future__ import annotations
@@ -18,6 +20,8 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_NAME = "libmqa_attn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+PEAKS_SRC = os.path.join(PKG_DIR, "peaks", "peaks.hip")
+PEAKS_LIB_PATH = os.path.join(PKG_DIR, "libmqa_peaks.so")
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
@@ -59,10 +63,20 @@ def _compile(src, extra):
     return obj, errs
 
 
+def _link(objs, path):
+    tmp = path + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{res.stderr}")
+    os.replace(tmp, path)
+
+
 def build_library(verbose=False, extra_flags=()):
-    """Compile all HIP sources and link the shared library. Returns its path."""
+    """Compile all HIP sources and link the shared libraries. Returns the
+    attention library's path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = _sources()
+    srcs = _sources() + [PEAKS_SRC]
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         results = list(ex.map(lambda s: _compile(s, list(extra_flags)), srcs))
     objs = [r[0] for r in results]
@@ -70,12 +84,8 @@ def build_library(verbose=False, extra_flags=()):
         for _, errs in results:
             if errs.strip():
                 print(errs, file=sys.stderr)
-    tmp = LIB_PATH + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError(f"link failed:\n{res.stderr}")
-    os.replace(tmp, LIB_PATH)
+    _link(objs[:-1], LIB_PATH)
+    _link(objs[-1:], PEAKS_LIB_PATH)
     return LIB_PATH
 
 

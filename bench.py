@@ -17,7 +17,10 @@ workload, inputs already resident in HBM:
                          the steps around the absorbed decode, batch 32,
                          H=128 (weights W_UK, W_UV read once per call)
   * mqa_prefill          the first workload with fp16 inputs and output
-all bf16 in (but the last), fp32 accumulation, 16-bit out.
+  * mqa_prefill          causal MQA in fp32 end to end, B=1, Hq=16, Hkv=1,
+                         T=128, d=512 (a latency-sized call on the fp32
+                         VALU kernel; its roofline is the fp32 vector rate)
+bf16 in (but the fp16 and fp32 ones), fp32 accumulation, 16-bit out.
 
 W untimed warm-up steps run first, extended (at most 400 steps) until they
 have kept the GPU busy for 1 s: a fresh device runs its first ~25 calls
@@ -29,10 +32,15 @@ with its roofline.  `roofline.traffic` is the HBM traffic per call measured
 with rocprofv3 counters (profiles/traffic.json), reported only while the
 kernel sources still hash to the value recorded with the counters.
 `cpu_baseline` times the fp64 numpy oracle on a bounded sample on the host
-cores.
+cores.  `attainable_peaks` are measured on the device by the probes of
+libmqa_peaks.so (bf16 MFMA loop at one and two waves per SIMD with the
+clock it ran at, HBM streaming read and copy, LDS reads); every roofline
+also carries `frac_attainable` against the matching measured ceiling.
+`host` records the ROCm, hipcc, torch and numpy versions, the GPU, the CPU
+model, its core count, this process's affinity and the BLAS threads.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--only name,name] [--copy-calibration MIB]
+                       [--only name,name] [--no-peaks] [--copy-calibration MIB]
 """
 
 from __future__ import annotations
@@ -67,7 +75,13 @@ ORDER = (
     ("mla_sparse_decode_bf16_b32_l32768_k2048", "mla_sparse_decode"),
     ("mla_step_proj_bf16_b32_h128", "mla_step_proj"),
     ("mqa_prefill_f16_b2_t4096", "f16_prefill"),
+    ("mqa_prefill_f32_b1_t128", "f32_prefill"),
 )
+
+PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector (256 CUs x 4 SIMD x 64 lanes x 2 flop x 2.4 GHz)
+
+# waves per SIMD of each prefill kernel (the matching measured MFMA ceiling)
+PREFILL_WAVES_PER_SIMD = {512: 1, 128: 2, 192: 2}
 
 
 def prefill_flops(B, Hq, T, D, causal=True, T_kv=None, DV=None, **_):
@@ -156,9 +170,55 @@ def cpu_baseline(q, k, v, scale, shape, min_seconds=10.0):
         if dt >= min_seconds:
             break
     fl = prefill_flops(1, shape["Hq"], shape["T"], shape["D"]) * reps
-    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+    threads = blas_threads()
+    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"causal MQA prefill, batch 0 of {shape['B']} ({shape['Hq']} heads x T={shape['T']} "
-                      f"x d={shape['D']}), fp64 numpy, {reps} passes in {dt:.1f} s"}
+                      f"x d={shape['D']}), fp64 numpy, {reps} passes in {dt:.1f} s",
+            "threads_note": f"numpy's BLAS ran on {threads} threads; the host has {os.cpu_count()} logical CPUs, "
+                            f"{len(os.sched_getaffinity(0)) if hasattr(os, 'sched_getaffinity') else '?'} "
+                            f"in this process's affinity"}
+
+
+def host_record():
+    """Versions and host facts for the record: ROCm, hipcc, torch (and its HIP),
+    the host's CPU model, core count, affinity and BLAS threads."""
+    import platform
+    import subprocess
+    rec = {"python": platform.python_version()}
+    try:
+        with open("/opt/rocm/.info/version") as fh:
+            rec["rocm"] = fh.read().strip()
+    except OSError:
+        rec["rocm"] = None
+    try:
+        out = subprocess.run(["hipcc", "--version"], capture_output=True, text=True, timeout=30).stdout
+        rec["hipcc"] = " | ".join(l.strip() for l in out.splitlines() if "version" in l.lower())[:200]
+    except Exception:
+        rec["hipcc"] = None
+    try:
+        import torch
+        rec["torch"] = torch.__version__
+        rec["torch_hip"] = getattr(torch.version, "hip", None)
+        if torch.cuda.is_available():
+            pr = torch.cuda.get_device_properties(0)
+            rec["gpu"] = f"{pr.name} ({getattr(pr, 'gcnArchName', '')}, {pr.multi_processor_count} CUs)"
+    except Exception:
+        pass
+    rec["numpy"] = np.__version__
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    rec["cpu_model"] = model
+    rec["cpu_count"] = os.cpu_count()
+    rec["cpu_affinity"] = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None
+    rec["blas_threads"] = blas_threads()
+    return rec
 
 
 def copy_calibration(mib, reps):
@@ -185,6 +245,7 @@ def main():
     ap.add_argument("--only", default="", help="comma-separated workload names (default: all)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the attainable-peak probes")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: every kernel here runs on a single MI355X "
@@ -217,8 +278,9 @@ def main():
             q, k, v = prefill_inputs(s["B"], s["Hq"], s["Hkv"], s["T"], s["D"], wl.dtype, seed=0, d_v=DV, T_kv=T_kv)
             dq, dk, dv = to_dev(q), to_dev(k), to_dev(v)
             out = torch.empty((s["B"], s["Hq"], s["T"], DV), dtype=dq.dtype, device=dev)
+            in_code = mqa.DTYPE_F32 if wl.dtype == "f32" else mqa.DTYPE_BF16
             ws = torch.empty(max(1, mqa.mqa_prefill_ex_workspace_size(s["B"], s["Hq"], s["Hkv"], s["T"], T_kv, s["D"],
-                                                                      DV, mqa.DTYPE_BF16)),
+                                                                      DV, in_code)),
                              dtype=torch.uint8, device=dev)
             sc = s["D"] ** -0.5
             if T_kv == s["T"] and DV == s["D"]:
@@ -227,7 +289,11 @@ def main():
             else:
                 calls[name] = (lambda dq=dq, dk=dk, dv=dv, out=out, ws=ws, sc=sc:
                                mqa.mqa_prefill_ex(dq, dk, dv, causal=True, scale=sc, out=out, workspace=ws))
-            work[name] = dict(flops=prefill_flops(**s), bytes=prefill_bytes(**s), bound="mfma", shape=s)
+            if wl.dtype == "f32":
+                work[name] = dict(flops=prefill_flops(**s), bytes=prefill_bytes(**s) * 2, bound="alu", shape=s)
+            else:
+                work[name] = dict(flops=prefill_flops(**s), bytes=prefill_bytes(**s), bound="mfma", shape=s,
+                                  waves_per_simd=PREFILL_WAVES_PER_SIMD.get(s["D"], 1))
             if name == ORDER[0][0]:
                 host[name] = (q, k, v, sc, s)
         elif wl.kind == "decode":
@@ -336,6 +402,17 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    peaks = {}
+    if not args.no_peaks:
+        from attention_mqa_gqa_amd import peaks as peak_probes
+        print("[bench] measuring attainable peaks ...", file=sys.stderr, flush=True)
+        peaks = peak_probes.measure()
+
+    def _attainable(roof, peak):
+        # the same achieved figure against the ceiling measured on this device
+        roof["attainable_peak"] = peak
+        roof["frac_attainable"] = round(roof["achieved"] / peak, 4) if peak else None
+
     traffic = load_traffic()
     sub = {}
     for name in names:
@@ -351,10 +428,15 @@ def main():
              "tflops": round(tflops, 2), "gbs": round(gbs, 1)}
         if w["bound"] == "mfma":
             r["roofline"] = roofline("mfma", tflops, PEAK_BF16_TFLOPS, "TFLOP/s", tr)
+            _attainable(r["roofline"], peaks.get(f"mfma_bf16_tflops_{w.get('waves_per_simd', 1)}wave"))
+        elif w["bound"] == "alu":
+            r["roofline"] = roofline("alu", tflops, PEAK_FP32_VALU_TFLOPS, "TFLOP/s", tr)
         else:
             r["roofline"] = roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", tr)
+            _attainable(r["roofline"], peaks.get("hbm_read_gbs"))
             if name.startswith("mla"):
                 r["roofline_mfma"] = roofline("mfma", tflops, PEAK_BF16_TFLOPS, "TFLOP/s", tr)
+                _attainable(r["roofline_mfma"], peaks.get("mfma_bf16_tflops_1wave"))
         if "mean_len" in w:
             r["mean_seq_len"] = w["mean_len"]
         if r["shape"].get("lengths") is not None:
@@ -391,6 +473,8 @@ def main():
             rec[role] = sub[name]
     if head in sub:
         rec["prefill"] = sub[head]
+    rec["attainable_peaks"] = peaks or None
+    rec["host"] = host_record()
     rec["cpu_baseline"] = None
     if not args.no_cpu_baseline and head in host:
         print("[bench] timing the fp64 oracle on a sample ...", file=sys.stderr, flush=True)
