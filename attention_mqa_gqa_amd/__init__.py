@@ -8,6 +8,8 @@ The entry points carry the C ABI's names (see ``include/mqa_attn.h``):
 * :func:`mqa_prefill_ex`       -- the same with T_q != T_kv (bottom-right
   causal) and d_v != d_qk (expanded MLA prefill);
 * :func:`mqa_decode`           -- one query token per sequence vs a KV cache;
+* :func:`mqa_decode_noalloc`   -- the same without workspace or allocation
+  (fixed per-device scratch), for callers that cannot allocate;
 * :func:`mla_decode_absorbed`  -- absorbed MLA decode over a latent cache;
 * :func:`mla_decode_sparse`    -- the same over selected (top-k) cache rows;
 * :func:`mla_absorb_query`, :func:`mla_cache_append`,
@@ -33,7 +35,9 @@ __all__ = [
     "mqa_prefill_ex",
     "mqa_prefill_ex_workspace_size",
     "mqa_decode",
+    "mqa_decode_noalloc",
     "mqa_decode_workspace_size",
+    "NOALLOC_SCRATCH_BYTES",
     "mla_decode_absorbed",
     "mla_decode_workspace_size",
     "mla_decode_sparse",
@@ -54,6 +58,9 @@ DTYPE_F32 = 0
 DTYPE_BF16 = 1
 DTYPE_F16 = 2
 
+# MQA_DECODE_NOALLOC_SCRATCH_BYTES: the fixed device scratch of mqa_decode_noalloc
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
 EXPORTED_SYMBOLS = (
     "mqa_attn_abi_version",
     "mqa_status_string",
@@ -64,6 +71,7 @@ EXPORTED_SYMBOLS = (
     "mqa_prefill_ex",
     "mqa_decode_workspace_size",
     "mqa_decode",
+    "mqa_decode_noalloc",
     "mla_decode_workspace_size",
     "mla_decode_absorbed",
     "mla_decode_sparse_workspace_size",
@@ -111,6 +119,8 @@ def _load():
     l.mqa_decode_workspace_size.argtypes = [i, i, i, i, i]
     l.mqa_decode.restype = i
     l.mqa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
+    l.mqa_decode_noalloc.restype = i
+    l.mqa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
     l.mla_decode_workspace_size.restype = sz
     l.mla_decode_workspace_size.argtypes = [i, i, i]
     l.mla_decode_absorbed.restype = i
@@ -361,6 +371,34 @@ def mqa_decode(q, k_cache, v_cache, seq_lens, scale=None, out=None, out_dtype=No
                         B, Hq, Hkv, L_max, D, scale, _dtype_code(q.dtype), _dtype_code(out.dtype),
                         _ptr(ws), wsb, _stream_ptr(stream, q.device))
     _check(st, "mqa_decode")
+    return out
+
+
+def mqa_decode_noalloc(q, k_cache, v_cache, seq_lens, out, scale=None, lse=None, stream=None):
+    """mqa_decode without a workspace and without allocating: the caller
+    passes `out` (and optionally `lse`); the split partials go to the
+    library's fixed per-device scratch (NOALLOC_SCRATCH_BYTES).  Raises
+    MqaError (status -3) when the call needs more scratch than that.  Calls
+    that may run concurrently on one device share the scratch and race."""
+    torch = _torch()
+    _require(q, "q", 3)
+    _require(k_cache, "k_cache", 4)
+    _require(v_cache, "v_cache", 4)
+    _same_dtype("q, k_cache, v_cache", q, k_cache, v_cache)
+    B, Hq, D = q.shape
+    Hkv, L_max = k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape != (B, Hkv, L_max, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [B, Hkv, L_max, D] matching q")
+    for t, nm in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _require_on(t, nm, q.device)
+    _check_index(seq_lens, "seq_lens", (B,), q.device)
+    _check_out(out, (B, Hq, D), q.device)
+    _check_lse(lse, (B, Hq), q.device)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    st = lib.mqa_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(out), _ptr(lse),
+                                B, Hq, Hkv, L_max, D, scale, _dtype_code(q.dtype), _dtype_code(out.dtype),
+                                _stream_ptr(stream, q.device))
+    _check(st, "mqa_decode_noalloc")
     return out
 
 

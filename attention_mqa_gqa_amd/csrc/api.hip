@@ -3,6 +3,7 @@
 // launchers in the kernel files receive only requests they support.
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/mqa_attn.h"
 #include "kernels.hpp"
@@ -42,6 +43,82 @@ bool prefill_supported(int d_qk, int d_v, int G, bool bf) {
 
 size_t decode_ws_bytes(int B, int Hq, int D, const DecodePlan& p) {
     return (size_t)B * Hq * p.n_split * ((size_t)D + 2) * sizeof(float);
+}
+
+// Fixed device scratch of mqa_decode_noalloc (its split partials), one copy
+// per device, held until the process ends.  In host code `scratch` only
+// names the symbol: its device address is looked up once per device with
+// hipGetSymbolAddress and kept in scratch_ptr; that pointer, never the
+// array's name, is what the kernels receive.
+static __device__ __align__(256) char scratch[MQA_DECODE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the
+// first call made with that device current).
+int current_scratch(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        g_last_hip_error = e;
+        return MQA_ERR_HIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return MQA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr) {
+            g_last_hip_error = e != hipSuccess ? e : hipErrorInvalidSymbol;
+            return MQA_ERR_HIP;
+        }
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return MQA_OK;
+}
+
+// Validation, plan and launch shared by mqa_decode and mqa_decode_noalloc.
+// get_ws(need, &ws, &bytes) is called only once every argument has been
+// accepted; it supplies the workspace (the caller's, or the device's fixed
+// scratch) or a status that ends the call.
+template <typename GetWs>
+int decode_impl(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens, void* out,
+                       float* lse, int B, int Hq, int Hkv, int max_len, int head_dim, float scale, int dtype,
+                       int out_dtype, GetWs get_ws, void* stream) {
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || max_len < 0 || head_dim <= 0) return MQA_ERR_INVALID_ARG;
+    if (Hq % Hkv != 0) return MQA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return MQA_ERR_INVALID_ARG;
+    if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return MQA_ERR_INVALID_ARG;
+    if (B == 0) return MQA_OK;
+    if (!q || !k_cache || !v_cache || !seq_lens || !out) return MQA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+        ((uintptr_t)seq_lens & 3u) || (lse && ((uintptr_t)lse & 3u)))
+        return MQA_ERR_INVALID_ARG;
+    const int G = Hq / Hkv;
+    if (!is16(dtype) || !valid_out(dtype, out_dtype)) return MQA_ERR_UNSUPPORTED;
+    if (head_dim != 128 && head_dim != 512) return MQA_ERR_UNSUPPORTED;
+    if (G > 16) return MQA_ERR_UNSUPPORTED;
+    if (max_len == 0) return MQA_ERR_INVALID_ARG;  // a cache with no rows cannot hold the current token
+    const DecodePlan plan = mqa::decode_plan(B, Hkv, max_len, head_dim);
+    const size_t need = decode_ws_bytes(B, Hq, head_dim, plan);
+    void* workspace = nullptr;
+    size_t workspace_bytes = 0;
+    const int st = get_ws(need, &workspace, &workspace_bytes);
+    if (st != MQA_OK) return st;
+    if (!workspace || workspace_bytes < need) return MQA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MQA_ERR_INVALID_ARG;
+    mqa::DecodeArgs a;
+    a.q = q; a.k = k_cache; a.v = v_cache; a.seq_lens = seq_lens; a.out = out; a.lse = lse;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.max_len = max_len; a.D = head_dim; a.G = G;
+    a.scale = scale; a.f16 = dtype == MQA_DTYPE_F16; a.out_f32 = out_dtype == MQA_DTYPE_F32;
+    a.part_o = (float*)workspace;
+    a.part_ml = (float*)workspace + (size_t)B * Hq * plan.n_split * head_dim;
+    a.plan = plan; a.stream = (hipStream_t)stream;
+    clear_stale_error();
+    return hip_status(mqa::decode_launch(a));
 }
 
 }  // namespace
@@ -132,33 +209,27 @@ size_t mqa_decode_workspace_size(int B, int Hq, int Hkv, int max_len, int head_d
 int mqa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens, void* out,
                float* lse, int B, int Hq, int Hkv, int max_len, int head_dim, float scale, int dtype, int out_dtype,
                void* workspace, size_t workspace_bytes, void* stream) {
-    if (B < 0 || Hq <= 0 || Hkv <= 0 || max_len < 0 || head_dim <= 0) return MQA_ERR_INVALID_ARG;
-    if (Hq % Hkv != 0) return MQA_ERR_INVALID_ARG;
-    if (!std::isfinite(scale) || !(scale > 0.f)) return MQA_ERR_INVALID_ARG;
-    if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return MQA_ERR_INVALID_ARG;
-    if (B == 0) return MQA_OK;
-    if (!q || !k_cache || !v_cache || !seq_lens || !out) return MQA_ERR_INVALID_ARG;
-    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
-        ((uintptr_t)seq_lens & 3u) || (lse && ((uintptr_t)lse & 3u)))
-        return MQA_ERR_INVALID_ARG;
-    const int G = Hq / Hkv;
-    if (!is16(dtype) || !valid_out(dtype, out_dtype)) return MQA_ERR_UNSUPPORTED;
-    if (head_dim != 128 && head_dim != 512) return MQA_ERR_UNSUPPORTED;
-    if (G > 16) return MQA_ERR_UNSUPPORTED;
-    if (max_len == 0) return MQA_ERR_INVALID_ARG;  // a cache with no rows cannot hold the current token
-    const DecodePlan plan = mqa::decode_plan(B, Hkv, max_len, head_dim);
-    const size_t need = decode_ws_bytes(B, Hq, head_dim, plan);
-    if (!workspace || workspace_bytes < need) return MQA_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return MQA_ERR_INVALID_ARG;
-    mqa::DecodeArgs a;
-    a.q = q; a.k = k_cache; a.v = v_cache; a.seq_lens = seq_lens; a.out = out; a.lse = lse;
-    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.max_len = max_len; a.D = head_dim; a.G = G;
-    a.scale = scale; a.f16 = dtype == MQA_DTYPE_F16; a.out_f32 = out_dtype == MQA_DTYPE_F32;
-    a.part_o = (float*)workspace;
-    a.part_ml = (float*)workspace + (size_t)B * Hq * plan.n_split * head_dim;
-    a.plan = plan; a.stream = (hipStream_t)stream;
-    clear_stale_error();
-    return hip_status(mqa::decode_launch(a));
+    return decode_impl(q, k_cache, v_cache, seq_lens, out, lse, B, Hq, Hkv, max_len, head_dim, scale, dtype, out_dtype,
+                       [&](size_t, void** ws, size_t* bytes) {
+                           *ws = workspace;
+                           *bytes = workspace_bytes;
+                           return (int)MQA_OK;
+                       },
+                       stream);
+}
+
+int mqa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens, void* out,
+                       float* lse, int B, int Hq, int Hkv, int max_len, int head_dim, float scale, int dtype,
+                       int out_dtype, void* stream) {
+    return decode_impl(q, k_cache, v_cache, seq_lens, out, lse, B, Hq, Hkv, max_len, head_dim, scale, dtype, out_dtype,
+                       [](size_t need, void** ws, size_t* bytes) {
+                           // too large for the fixed scratch: rejected before
+                           // anything touches the device
+                           if (need > MQA_DECODE_NOALLOC_SCRATCH_BYTES) return (int)MQA_ERR_WORKSPACE;
+                           *bytes = MQA_DECODE_NOALLOC_SCRATCH_BYTES;
+                           return current_scratch(ws);
+                       },
+                       stream);
 }
 
 size_t mla_decode_workspace_size(int B, int H, int max_len) {

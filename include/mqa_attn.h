@@ -169,6 +169,35 @@ int mqa_decode(const void* q, const void* k_cache, const void* v_cache,
                int dtype, int out_dtype,
                void* workspace, size_t workspace_bytes, void* stream);
 
+/* -------------------------------------------- decode without allocation
+ * mqa_decode for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, semantics, kernels and results
+ * as mqa_decode (bit for bit), minus the workspace: the chunk partials go
+ * to a fixed scratch array of MQA_DECODE_NOALLOC_SCRATCH_BYTES (64 MiB) in
+ * the library's device memory, one per device, resolved on the first call
+ * made with that device current and held until the process ends.  The call
+ * allocates nothing (no hipMalloc / hipFree, no allocating library call).
+ * A call whose partials would exceed the scratch, i.e.
+ * mqa_decode_workspace_size(B, Hq, Hkv, max_len, head_dim) >
+ * MQA_DECODE_NOALLOC_SCRATCH_BYTES, returns MQA_ERR_WORKSPACE and enqueues
+ * nothing.  For scale: MQA batch 64 x 16 heads at d 512 needs 8 MiB with an
+ * 8192-row cache and 32 MiB with a 65536-row one; GQA batch 128 x 64 heads
+ * at d 128 with a 16384-row cache needs 4 MiB; MQA batch 2048 x 16 heads at
+ * d 512 (64.25 MiB) is refused.
+ * Every call on one device shares that device's scratch: calls that can run
+ * at the same time on one device (different streams, or graphs replayed
+ * concurrently) race on it and must be serialised by the caller.  Nothing
+ * in the scratch needs to start at any particular value (each partial is
+ * written before it is read).
+ */
+#define MQA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+int mqa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* seq_lens, void* out, float* lse,
+                       int B, int Hq, int Hkv, int max_len, int head_dim, float scale,
+                       int dtype, int out_dtype, void* stream);
+
 /* ----------------------------------------------------- MLA absorbed decode
  * Decode for multi-head latent attention in the absorbed form.  Every cached
  * token is one row [c_kv (512) | k_pe (64)] = 576 values shared by all heads.

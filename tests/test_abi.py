@@ -28,7 +28,7 @@ def _declared_functions():
 
 def test_header_functions_are_exported():
     names = _declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     assert sorted(names) == sorted(mqa.EXPORTED_SYMBOLS)
     for n in names:
         assert hasattr(lib, n), n
@@ -258,6 +258,7 @@ def test_launch_failure_is_reported_as_hip_error():
     assert lib.mqa_last_hip_error_name() not in (b"hipSuccess", b"")
     dws = lib.mqa_decode_workspace_size(2, 16, 1, 64, 512)
     assert lib.mqa_decode(P, P, P, P, P, None, 2, 16, 1, 64, 512, 0.05, BF16, BF16, P, dws, None) == -4
+    assert lib.mqa_decode_noalloc(P, P, P, P, P, None, 2, 16, 1, 64, 512, 0.05, BF16, BF16, None) == -4
     mws = lib.mla_decode_workspace_size(2, 16, 64)
     assert lib.mla_decode_absorbed(P, P, P, P, None, 2, 16, 64, 0.07, BF16, BF16, P, mws, None) == -4
     name = lib.mqa_last_hip_error_name()
@@ -283,3 +284,17 @@ def test_peaks_header_functions_are_exported():
     assert pl.mqa_peak_hbm_read(MIS, 1 << 20, P, None) == -1
     assert pl.mqa_peak_hbm_copy(P, MIS, 1 << 20, None) == -1
     assert pl.mqa_peak_lds_read(17, 10, P, None) == -1
+
+
+def test_decode_noalloc_rejections():
+    """The allocation-free decode validates like mqa_decode, and refuses a
+    call whose partials exceed its fixed scratch before touching the device."""
+    f = lib.mqa_decode_noalloc
+    assert f(P, P, P, P, P, None, 2, 16, 3, 64, 512, 0.05, BF16, BF16, None) == INVALID
+    assert f(P, P, P, None, P, None, 2, 16, 1, 64, 512, 0.05, BF16, BF16, None) == INVALID
+    assert f(P, P, P, P, MIS, None, 2, 16, 1, 64, 512, 0.05, BF16, BF16, None) == INVALID
+    assert f(P, P, P, P, P, None, 2, 64, 1, 64, 128, 0.05, BF16, BF16, None) == UNSUPPORTED
+    assert f(None, None, None, None, None, None, 0, 16, 1, 64, 512, 0.05, BF16, BF16, None) == OK
+    assert lib.mqa_decode_workspace_size(2048, 16, 1, 4096, 512) > mqa.NOALLOC_SCRATCH_BYTES
+    assert f(P, P, P, P, P, None, 2048, 16, 1, 4096, 512, 0.05, BF16, BF16, None) == WORKSPACE
+    assert lib.mqa_decode_workspace_size(64, 16, 1, 65536, 512) <= mqa.NOALLOC_SCRATCH_BYTES
