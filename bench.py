@@ -41,6 +41,7 @@ model, its core count, this process's affinity and the BLAS threads.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--only name,name] [--no-peaks] [--copy-calibration MIB]
+       python bench.py --counters-summary DIR [DIR ...]   (rocprofv3 --pmc output)
 """
 
 from __future__ import annotations
@@ -221,6 +222,72 @@ def host_record():
     return rec
 
 
+def counters_summary(dirs, num_xcd=8, num_cu=256, simds_per_cu=4):
+    """Summarise rocprofv3 --pmc runs (counter_collection CSVs under `dirs`)
+    per kernel: the mean of every counter per dispatch and derived rates.
+
+    Normalisation (one dispatch): GRBM_GUI_ACTIVE is summed over the XCDs,
+    so cycles = GRBM_GUI_ACTIVE / XCDs and clock = cycles / duration;
+    SQ_VALU_MFMA_BUSY_CYCLES is summed over all SIMDs (MFMA busy = it /
+    (SIMDs x cycles)); SQ_*_CYCLES / SQ_ACTIVE_* / SQ_WAIT_* count in units
+    of 4 cycles summed over waves (per-wave share = 4 x value / waves /
+    wave lifetime); LDS counters are summed over CUs."""
+    import csv
+    import glob
+    per = {}
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    k = r["Kernel_Name"]
+                    c = per.setdefault(k, {})
+                    c.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                    if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                        c.setdefault("_dur_ns", []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    lines = []
+    for k in sorted(per):
+        c = {n: float(np.mean(v)) for n, v in per[k].items()}
+        if "GRBM_GUI_ACTIVE" not in c or c.get("SQ_WAVES", 1) < 64:
+            continue
+        short = k.split("(")[0][:110]
+        cyc = c["GRBM_GUI_ACTIVE"] / num_xcd
+        dur = c["_dur_ns"] * 1e-9
+        simd_cycles = cyc * num_cu * simds_per_cu
+        cu_cycles = cyc * num_cu
+        lines.append(f"kernel {short}")
+        # (the clock is meaningful only for long dispatches: GRBM_GUI_ACTIVE
+        # also counts the dispatch's start-up and drain)
+        clock = f" -> clock {cyc / dur / 1e9:.3f} GHz" if dur > 50e-6 else ""
+        lines.append(f"  dispatches {len(per[k]['GRBM_GUI_ACTIVE'])}, mean duration {dur * 1e6:.1f} us, "
+                     f"GPU cycles {cyc:.0f}{clock}")
+        der = []
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+            der.append(("MFMA busy (of SIMD cycles)", c["SQ_VALU_MFMA_BUSY_CYCLES"] / simd_cycles))
+        waves = c.get("SQ_WAVES")
+        if waves and "SQ_WAVE_CYCLES" in c:
+            life = 4 * c["SQ_WAVE_CYCLES"] / waves
+            der.append(("wave lifetime (cycles)", life))
+            for n in ("SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_MISC",
+                      "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS"):
+                if n in c:
+                    der.append((f"{n} (share of wave time)", 4 * c[n] / waves / life))
+        if "SQ_LDS_IDX_ACTIVE" in c:
+            der.append(("LDS active (of CU cycles)", c["SQ_LDS_IDX_ACTIVE"] / cu_cycles))
+        if "SQ_LDS_BANK_CONFLICT" in c:
+            der.append(("LDS bank-conflict cycles (of CU cycles)", c["SQ_LDS_BANK_CONFLICT"] / cu_cycles))
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in c:
+            der.append(("VALU issued beside an MFMA (of SIMD cycles)", c["SQ_VALU_MFMA_COEXEC_CYCLES"] / simd_cycles))
+        if waves:
+            for n in ("SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_VMEM", "SQ_INSTS_SALU"):
+                if n in c:
+                    der.append((f"{n} per wave", c[n] / waves))
+        for name, val in der:
+            lines.append(f"  {name:48s} {val:12.3f}")
+        raw = ", ".join(f"{n}={v:.4g}" for n, v in sorted(c.items()) if not n.startswith("_"))
+        lines.append(f"  raw means per dispatch: {raw}")
+    return "\n".join(lines)
+
+
 def copy_calibration(mib, reps):
     """A plain device copy of known size (for scaling the HBM counters)."""
     import torch
@@ -246,11 +313,16 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--no-peaks", action="store_true", help="skip the attainable-peak probes")
+    ap.add_argument("--counters-summary", nargs="+", default=None, metavar="DIR",
+                    help="only summarise rocprofv3 --pmc output directories (no GPU needed)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: every kernel here runs on a single MI355X "
               "(sharding across GPUs is a design note, not built). Run with --gpus 1.", file=sys.stderr)
         return 2
+    if args.counters_summary:
+        print(counters_summary(args.counters_summary))
+        return 0
     if args.copy_calibration:
         return copy_calibration(args.copy_calibration, max(args.steps, 1))
 
