@@ -288,6 +288,116 @@ def counters_summary(dirs, num_xcd=8, num_cu=256, simds_per_cu=4):
     return "\n".join(lines)
 
 
+# The kernels each entry-point call dispatches, in order (substrings of the
+# demangled names in rocprofv3 output); used to assign profiled dispatches to
+# workloads by their order within a step.
+CALL_KERNELS = {
+    "mqa_prefill_bf16_b2_t4096": ("kv_pack_kernel<512", "prefill_bf16_kernel<512"),
+    "mqa_decode_bf16_b64_l8192": ("decode_split_kernel<512", "lse_merge_kernel<512"),
+    "gqa_prefill_bf16_b1_t8192": ("kv_pack_kernel<128", "prefill_bf16_kernel<128"),
+    "gqa_decode_bf16_b128_l1024to16384": ("decode_split_kernel<128", "lse_merge_kernel<128"),
+    "mla_decode_bf16_b32_l32768": ("mla_decode_kernel<false", "lse_merge_kernel<512"),
+    "mla_prefill_bf16_b1_h128_t8192": ("kv_pack_kernel<192", "prefill_bf16_kernel<192"),
+    "mqa_chunk_prefill_bf16_b2_q1024_kv8192": ("kv_pack_kernel<512", "prefill_bf16_kernel<512"),
+    "mla_sparse_decode_bf16_b32_l32768_k2048": ("mla_decode_kernel<true", "lse_merge_kernel<512"),
+    "mla_step_proj_bf16_b32_h128": ("mla_absorb_kernel", "mla_cache_append_kernel", "mla_out_proj_kernel"),
+    "mqa_prefill_f16_b2_t4096": ("kv_pack_kernel<512", "prefill_bf16_kernel<512"),
+    "mqa_prefill_f32_b1_t128": ("prefill_f32_kernel<512",),
+}
+
+
+def _read_csvs(d, suffix):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def assign_dispatches(kernel_names, names=None):
+    """Assign an ordered list of dispatched kernel names to (workload, kernel
+    slot) by walking the per-step kernel sequence of the bench (dispatches
+    that do not fit the sequence, e.g. set-up calls, are skipped).  Returns a
+    list of (workload, slot) or None per dispatch."""
+    names = [n for n, _ in ORDER if names is None or n in names]
+    seq = [(n, i, pat) for n in names for i, pat in enumerate(CALL_KERNELS[n])]
+    out, p = [], 0
+    for k in kernel_names:
+        if "mqa::" in k and seq[p][2] in k:
+            out.append((seq[p][0], seq[p][1]))
+            p = (p + 1) % len(seq)
+        else:
+            out.append(None)
+    return out
+
+
+def kernel_trace_summary(d):
+    """Per-workload, per-kernel durations from a rocprofv3 --kernel-trace run
+    of bench.py (all steps, warm-up included)."""
+    rows = _read_csvs(d, "kernel_trace.csv")
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    names = [r["Kernel_Name"] for r in rows]
+    asg = assign_dispatches(names)
+    per = {}
+    for r, a in zip(rows, asg):
+        if a is None:
+            continue
+        per.setdefault(a, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+    lines = [f"{'workload':40s} {'kernel':84s} {'calls':>6s} {'avg us':>9s} {'min us':>9s} {'max us':>9s}"]
+    for n, _ in ORDER:
+        for i, pat in enumerate(CALL_KERNELS[n]):
+            v = per.get((n, i))
+            if not v:
+                continue
+            kname = next(k for k, a in zip(names, asg) if a == (n, i)).split("(")[0].replace("void ", "").replace("mqa::", "")
+            lines.append(f"{n:40s} {kname[:84]:84s} {len(v):6d} {np.mean(v):9.1f} {np.min(v):9.1f} {np.max(v):9.1f}")
+    return "\n".join(lines), per
+
+
+def traffic_summary(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, cal_bytes):
+    """HBM bytes per entry-point call from rocprofv3 FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch, one counter per run), each scaled by what the same
+    counter reads for a plain device copy of `cal_bytes` (read factor =
+    cal_bytes / (1024 x FETCH_SIZE of the copy), write factor likewise)."""
+    def per_dispatch(d, counter):
+        rows = [r for r in _read_csvs(d, "counter_collection.csv") if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        return [(r["Kernel_Name"], float(r["Counter_Value"])) for r in rows]
+
+    def cal_factor(d, counter):
+        vals = [v for k, v in per_dispatch(d, counter)]
+        big = max(vals)
+        return cal_bytes / (1024.0 * big)
+
+    rf, wf = cal_factor(cal_fetch_dir, "FETCH_SIZE"), cal_factor(cal_write_dir, "WRITE_SIZE")
+    calls = {}
+    for d, counter, f in ((fetch_dir, "FETCH_SIZE", rf), (write_dir, "WRITE_SIZE", wf)):
+        disp = per_dispatch(d, counter)
+        asg = assign_dispatches([k for k, _ in disp])
+        acc = {}
+        for (k, v), a in zip(disp, asg):
+            if a is not None:
+                acc.setdefault(a, []).append(v * 1024.0 * f)
+        for (n, i), v in acc.items():
+            calls.setdefault(n, {}).setdefault(counter, {})[i] = float(np.mean(v))
+    per_call = {n: int(round(sum(c.get("FETCH_SIZE", {}).values()) + sum(c.get("WRITE_SIZE", {}).values())))
+                for n, c in calls.items()}
+    lines = [f"{'workload':40s} {'kernel':26s} {'read MB':>9s} {'write MB':>9s}"]
+    for n, _ in ORDER:
+        for i, pat in enumerate(CALL_KERNELS[n]):
+            c = calls.get(n, {})
+            if i in c.get("FETCH_SIZE", {}):
+                kname = pat.split("<")[0]
+                lines.append(f"{n:40s} {kname:26s} {c['FETCH_SIZE'].get(i, 0) / 1e6:9.1f} "
+                             f"{c.get('WRITE_SIZE', {}).get(i, 0) / 1e6:9.1f}")
+    return {"source_sha256": source_hash(), "read_factor": round(rf, 4), "write_factor": round(wf, 4),
+            "per_call_bytes": per_call, "table": "\n".join(lines),
+            "per_call_detail": {n: {k: {str(i): round(x) for i, x in v.items()} for k, v in c.items()}
+                                for n, c in calls.items()}}
+
+
 def copy_calibration(mib, reps):
     """A plain device copy of known size (for scaling the HBM counters)."""
     import torch
@@ -315,6 +425,12 @@ def main():
     ap.add_argument("--no-peaks", action="store_true", help="skip the attainable-peak probes")
     ap.add_argument("--counters-summary", nargs="+", default=None, metavar="DIR",
                     help="only summarise rocprofv3 --pmc output directories (no GPU needed)")
+    ap.add_argument("--trace-summary", default=None, metavar="DIR",
+                    help="only summarise a rocprofv3 --kernel-trace run of this bench per workload")
+    ap.add_argument("--traffic-summary", nargs=5, default=None,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR", "CAL_MIB"),
+                    help="only compute per-call HBM bytes from FETCH_SIZE / WRITE_SIZE runs and a copy "
+                         "calibration, and write profiles/traffic.json")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: every kernel here runs on a single MI355X "
@@ -322,6 +438,22 @@ def main():
         return 2
     if args.counters_summary:
         print(counters_summary(args.counters_summary))
+        return 0
+    if args.trace_summary:
+        print(kernel_trace_summary(args.trace_summary)[0])
+        return 0
+    if args.traffic_summary:
+        fd, wd, cfd, cwd, mib = args.traffic_summary
+        t = traffic_summary(fd, wd, cfd, cwd, int(mib) << 20)
+        t["note"] = ("HBM bytes per entry-point call (all its kernels) from rocprofv3 FETCH_SIZE / WRITE_SIZE, "
+                     "scaled by the factors a plain device copy gives; bench.py reports them only while the "
+                     "kernel sources hash to source_sha256")
+        table = t.pop("table")
+        with open(TRAFFIC_FILE, "w") as fh:
+            json.dump(t, fh, indent=1)
+        print(f"read factor {t['read_factor']}, write factor {t['write_factor']}, "
+              f"sources sha256 {t['source_sha256']}")
+        print(table)
         return 0
     if args.copy_calibration:
         return copy_calibration(args.copy_calibration, max(args.steps, 1))

@@ -47,3 +47,25 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_dispatch_assignment_walks_the_step_order():
+    # two steps of two workloads, with set-up and library kernels between
+    names = ["mqa_prefill_bf16_b2_t4096", "mqa_decode_bf16_b64_l8192"]
+    step = ["void mqa::kv_pack_kernel<512, 512, 32>(...)", "at::native::fill(...)",
+            "void mqa::prefill_bf16_kernel<512, 512, 1, 4, 32, true, false, false>(...)",
+            "void mqa::decode_split_kernel<512, 1, 4, false>(...)",
+            "void mqa::lse_merge_kernel<512, false, false>(...)"]
+    seq = ["at::native::copy(...)"] + step + step
+    got = bench.assign_dispatches(seq, names)
+    want_step = [(names[0], 0), None, (names[0], 1), (names[1], 0), (names[1], 1)]
+    assert got == [None] + want_step + want_step
+
+
+def test_dispatch_assignment_keeps_shared_kernel_names_apart():
+    # the chunked prefill dispatches the same kernels as the full prefill;
+    # only the position in the step tells them apart
+    names = ["mqa_prefill_bf16_b2_t4096", "mqa_chunk_prefill_bf16_b2_q1024_kv8192"]
+    k = ["mqa::kv_pack_kernel<512, 512, 32>", "mqa::prefill_bf16_kernel<512, 512, 1, 4, 32, true, false, false>"]
+    got = bench.assign_dispatches(k * 4, names)
+    assert got == [(names[0], 0), (names[0], 1), (names[1], 0), (names[1], 1)] * 2
