@@ -339,10 +339,14 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
         __syncthreads();
         for (int it = 0; it < n_tiles; ++it) {
             // copies of tile t+2 spread over the score MFMAs, one every
-            // four steps
-            const bool copy_next = it + 2 < n_tiles;
+            // four steps.  They are issued on every iteration, also past the
+            // last tile (their rows clamp to the chunk's last row and land in
+            // a stage nothing reads again): a branch here would split the
+            // MFMA chain into short scheduling regions, and the K operand
+            // reads would then go out only one or two MFMAs ahead of use
+            // (3 % slower)
             f32x16 sn = scores(smem + ((it + 1) % kNS) * kStageB, [&](int ks) {
-                if (ks % 4 == 0 && ks / 4 < kCopiesPerWave && copy_next) issue_one(it + 2, ks / 4);
+                if (ks % 4 == 0 && ks / 4 < kCopiesPerWave) issue_one(it + 2, ks / 4);
             });
             // P(t).V(t) as in pv_tile (written out: the register allocator
             // fits this loop without spills only in this form), with the

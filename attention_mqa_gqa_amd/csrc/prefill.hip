@@ -235,9 +235,14 @@ __global__ __launch_bounds__(NW * 64, (DK == 512 ? 1 : 8 / NW)) void prefill_bf1
     const uint32_t lds_base = lds_addr(smem);
     const uint32_t lane16 = (uint32_t)lane * 16u;
     // copy group g (of FK / 4) of a padded K tile: four padded 1 KB rows,
-    // identical in the stream and in LDS, four copies per M0 write
+    // identical in the stream and in LDS, four copies per M0 write.  The
+    // grouped copies (padded K, V^T) sit inside the MFMA chains and are
+    // issued on every iteration, also for tiles past the last one: those
+    // read the last tile again into a stage that nothing reads afterwards
+    // (bit-identical results; a branch would cut the chain into separate
+    // scheduling regions, 1.2 % slower at d_qk = 512)
     auto issue_k_group = [&](int tile, int g) {
-        const char* src = KVbh + (size_t)tile * TILE_B;
+        const char* src = KVbh + (size_t)min(tile, n_tiles - 1) * TILE_B;
         const uint32_t dst = lds_base + (uint32_t)((tile & 1) * KSTAGE_B);
         const int row = (g * NW + w) * 4;
         if constexpr (KPAD) copy4_to_lds_async<KROW_B>(src + row * KROW_B, lane16, dst + (uint32_t)(row * KROW_B));
@@ -280,7 +285,7 @@ __global__ __launch_bounds__(NW * 64, (DK == 512 ? 1 : 8 / NW)) void prefill_bf1
     // copy group g (of LHV / 4) of a V^T tile: V^T tiles are contiguous in
     // both places, so each wave copies runs of 4 KB, four copies per M0 write
     auto issue_v_group = [&](int tile, int g) {
-        const char* src = KVbh + (size_t)tile * TILE_B + KSTREAM_B;
+        const char* src = KVbh + (size_t)min(tile, n_tiles - 1) * TILE_B + KSTREAM_B;
         const uint32_t dst = lds_base + (uint32_t)(2 * KSTAGE_B + (tile & 1) * VSTAGE_B);
         const int inst = (g * NW + w) * 4;
         copy4_to_lds_async<1024>(src + inst * 1024, lane16, dst + (uint32_t)inst * 1024u);
@@ -433,7 +438,7 @@ __global__ __launch_bounds__(NW * 64, (DK == 512 ? 1 : 8 / NW)) void prefill_bf1
             for (int ks = 0; ks < KS; ++ks) {
                 // padded K: the copy groups spread evenly over the phase
                 if constexpr (KPAD) {
-                    if (ks % (KS / (FK / 4)) == 0 && it + 2 < n_tiles) issue_k_group(it + 2, ks / (KS / (FK / 4)));
+                    if (ks % (KS / (FK / 4)) == 0) issue_k_group(it + 2, ks / (KS / (FK / 4)));
                 }
                 const bf16x8 a = abuf[ks % PF];
                 if (ks + PF < KS) abuf[ks % PF] = kread(kst, ks + PF);
@@ -493,7 +498,7 @@ __global__ __launch_bounds__(NW * 64, (DK == 512 ? 1 : 8 / NW)) void prefill_bf1
             for (int st = 0; st < NSTEP_PV; ++st) {
                 // V(t+1) in this phase: the copy groups spread evenly over it
                 if constexpr (V_IN_B) {
-                    if (st % (NSTEP_PV / (LHV / 4)) == 0 && has_next) issue_v_group(it + 1, st / (NSTEP_PV / (LHV / 4)));
+                    if (st % (NSTEP_PV / (LHV / 4)) == 0) issue_v_group(it + 1, st / (NSTEP_PV / (LHV / 4)));
                 }
                 const bf16x8 a = vbuf[st % PF];
                 if (st + PF < NSTEP_PV) vbuf[st % PF] = *(const bf16x8*)vaddr(st + PF);
@@ -543,6 +548,7 @@ __global__ __launch_bounds__(NW * 64, (DK == 512 ? 1 : 8 / NW)) void prefill_bf1
         body(it, sA, sB);
         if (it + 1 < n_tiles) body(it + 1, sB, sA);
     }
+    wait_vmcnt<0>();    // the copies past the last tile
 
     // ---- epilogue: normalise, store ------------------------------------------
     mfma_acc_drain();
