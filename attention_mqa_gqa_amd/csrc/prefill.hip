@@ -581,89 +581,166 @@ __global__ __launch_bounds__(NW * 64, (DK == 512 ? 1 : 8 / NW)) void prefill_bf1
 }
 
 // ---------------------------------------------------------------------------
-// fp32 prefill: genuine fp32 end to end (fp32 FMA, fp32 exp2).  One wave
-// handles four consecutive query tokens of one head; lanes split the widths
-// (DK/64 query/key and DV/64 value elements per lane).  Online softmax per
-// row.  Causal: query token i sees keys j <= i + q_off.
+// fp32 prefill on the fp32 MFMA (v_mfma_f32_16x16x4_f32: fp32 products and
+// fp32 accumulation), fp32 exp2.  One workgroup = 16 consecutive rows of one
+// (batch, KV head), row rho = token * G + head within the group (any G), so
+// every K/V tile staged in LDS serves all the group's heads.  Key tiles of
+// 16.  The four waves split the widths: wave w holds dims
+// [w DK/4, (w+1) DK/4) of Q^T (the contraction slice of its partial scores)
+// and value dims [w DV/4, (w+1) DV/4) of O^T.  The partial scores are summed
+// through LDS in wave order, so every wave holds the same full scores and
+// runs the same online softmax on them.
+// 16x16x4 f32 layouts (wave64): A[m][k] in lane 16k + m, B[k][n] in lane
+// 16k + n, D[m][n] accumulator i of lane 16(m/4) + n with i = m % 4.
+// Scores are S^T (m = key, n = row).  Row m of the A operand carries key
+// 4(m%4) + m/4 of the tile, so accumulator i of lane group g holds key
+// 4i + g: the B operand (P^T, k = g) of P.V step i, with no data movement.
+// K rows are padded by 16 bytes and V rows by 64 in LDS, which spreads both
+// operand read patterns over distinct banks.
 // ---------------------------------------------------------------------------
+constexpr int kF32Rows = 16;   // rows per workgroup
+constexpr int kF32Kt = 16;     // keys per tile
+
 template <int DK, int DV, bool CAUSAL>
 __global__ __launch_bounds__(256) void prefill_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                           const float* __restrict__ V, float* __restrict__ Out,
-                                                          float* __restrict__ Lse, int Hq, int Hkv, int Tq, int Tkv,
-                                                          int q_off, int G, float scale_log2) {
-    constexpr int EK = DK / 64;
-    constexpr int EV = DV / 64;
-    constexpr int RPW = 4;
+                                                          float* __restrict__ Lse, int Hq, int Tq, int Tkv,
+                                                          int q_off, int G, int n_blk, float scale_log2) {
+    constexpr int QS = DK / 4;            // contraction slice per wave
+    constexpr int KSW = QS / 4;           // MFMA steps of a partial score
+    constexpr int VS = DV / 4;            // value dims per wave
+    constexpr int MTV = VS / 16;          // O^T tiles per wave
+    constexpr int KROW = DK + 4;          // LDS row strides (floats)
+    constexpr int VROW = DV + 16;
+    constexpr int KTILE = kF32Kt * KROW;
+    constexpr int VTILE = kF32Kt * VROW;
+    constexpr int CK = DK / 64;           // 16-byte chunks per thread per K tile
+    constexpr int CV = DV / 64;
+    static_assert(DK % 64 == 0 && DV % 64 == 0, "widths are multiples of 64");
+    __shared__ __attribute__((aligned(16))) float lds[2 * KTILE + 2 * VTILE + 4 * 64 * 4];
+    float* const kst = lds;                              // [2][KTILE]
+    float* const vst = lds + 2 * KTILE;                  // [2][VTILE]
+    float* const xs = lds + 2 * KTILE + 2 * VTILE;       // partial scores [wave][lane][4]
+
+    const int tid = (int)threadIdx.x;
     const int lane = lane_id();
     const int w = wave_id();
-    const int h = blockIdx.y;
-    const int b = blockIdx.z;
-    const int hk = h / G;
-    const int tb = CAUSAL ? ((int)gridDim.x - 1 - (int)blockIdx.x) : (int)blockIdx.x;
-    const int tbase = tb * (4 * RPW) + w * RPW;
-    if (tbase >= Tq) return;
+    const int g = lane >> 4, n = lane & 15;
+    const int hk = blockIdx.y, b = blockIdx.z;
+    const int blk = CAUSAL ? (n_blk - 1 - (int)blockIdx.x) : (int)blockIdx.x;   // heaviest first
+    const long long rho0 = (long long)blk * kF32Rows;
+    const long long rho = rho0 + n;
+    const int tok = (int)(rho / G);
+    const int head = hk * G + (int)(rho % G);
+    const bool row_ok = tok < Tq;
+    const int t_last = (int)min((long long)Tq - 1, (rho0 + kF32Rows - 1) / G);
+    const int n_kv = (Tkv + kF32Kt - 1) / kF32Kt;
+    const int n_tiles = CAUSAL ? min((t_last + q_off) / kF32Kt + 1, n_kv) : n_kv;
+    const int Hkv = (int)gridDim.y;
 
+    // B operands of the partial scores: lane (g, n) holds Q[row n][w QS + 4s + g]
+    float qv[KSW];
+    {
+        const float* qrow = Q + (((size_t)b * Hq + head) * Tq + (row_ok ? tok : 0)) * DK + w * QS + g;
+#pragma unroll
+        for (int s = 0; s < KSW; ++s) qv[s] = row_ok ? qrow[4 * s] : 0.f;
+    }
     const float* Kbh = K + ((size_t)b * Hkv + hk) * (size_t)Tkv * DK;
     const float* Vbh = V + ((size_t)b * Hkv + hk) * (size_t)Tkv * DV;
-    float q[RPW][EK], o[RPW][EV], m[RPW], l[RPW];
+    // tile t through registers: thread chunk c = tid + 256 r is key c / (D/4),
+    // 16-byte column c % (D/4); keys past the end read the last key (masked)
+    u32x4 kr[CK], vr[CV];
+    auto load_tile = [&](int t) {
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-        const int t = min(tbase + r, Tq - 1);
-        const float* qrow = Q + (((size_t)b * Hq + h) * Tq + t) * DK + lane * EK;
-#pragma unroll
-        for (int e = 0; e < EK; ++e) q[r][e] = qrow[e];
-#pragma unroll
-        for (int e = 0; e < EV; ++e) o[r][e] = 0.f;
-        m[r] = -INFINITY;
-        l[r] = 0.f;
-    }
-    const int jmax = CAUSAL ? min(tbase + RPW - 1 + q_off, Tkv - 1) : Tkv - 1;
-    for (int j = 0; j <= jmax; ++j) {
-        float kv[EK], vv[EV];
-#pragma unroll
-        for (int e = 0; e < EK; ++e) kv[e] = Kbh[(size_t)j * DK + lane * EK + e];
-#pragma unroll
-        for (int e = 0; e < EV; ++e) vv[e] = Vbh[(size_t)j * DV + lane * EV + e];
-        float dot[RPW];
-#pragma unroll
-        for (int r = 0; r < RPW; ++r) {
-            float acc = 0.f;
-#pragma unroll
-            for (int e = 0; e < EK; ++e) acc = fmaf(q[r][e], kv[e], acc);
-            dot[r] = acc;
+        for (int r = 0; r < CK; ++r) {
+            const int c = tid + 256 * r;
+            const int j = min(t * kF32Kt + c / (DK / 4), Tkv - 1);
+            kr[r] = ldg16(Kbh + (size_t)j * DK + (c % (DK / 4)) * 4);
         }
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1)
-#pragma unroll
-            for (int r = 0; r < RPW; ++r) dot[r] += __shfl_xor(dot[r], off);
-#pragma unroll
-        for (int r = 0; r < RPW; ++r) {
-            if (CAUSAL && j > tbase + r + q_off) continue;
-            const float sc = dot[r] * scale_log2;
-            const float mnew = fmaxf(m[r], sc);
-            const float alpha = fast_exp2(m[r] - mnew);
-            const float p = fast_exp2(sc - mnew);
-            l[r] = l[r] * alpha + p;
-#pragma unroll
-            for (int e = 0; e < EV; ++e) o[r][e] = fmaf(p, vv[e], o[r][e] * alpha);
-            m[r] = mnew;
+        for (int r = 0; r < CV; ++r) {
+            const int c = tid + 256 * r;
+            const int j = min(t * kF32Kt + c / (DV / 4), Tkv - 1);
+            vr[r] = ldg16(Vbh + (size_t)j * DV + (c % (DV / 4)) * 4);
         }
-    }
+    };
+    auto store_tile = [&](int stage) {
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-        const int t = tbase + r;
-        if (t >= Tq) continue;
-        const size_t row = ((size_t)b * Hq + h) * Tq + t;
-        const float inv = 1.f / l[r];
+        for (int r = 0; r < CK; ++r) {
+            const int c = tid + 256 * r;
+            *(u32x4*)(kst + stage * KTILE + (c / (DK / 4)) * KROW + (c % (DK / 4)) * 4) = kr[r];
+        }
 #pragma unroll
-        for (int e = 0; e < EV; ++e) Out[row * DV + lane * EV + e] = o[r][e] * inv;
-        if (Lse != nullptr && lane == 0) Lse[row] = m[r] * kLn2 + logf(l[r]);
+        for (int r = 0; r < CV; ++r) {
+            const int c = tid + 256 * r;
+            *(u32x4*)(vst + stage * VTILE + (c / (DV / 4)) * VROW + (c % (DV / 4)) * 4) = vr[r];
+        }
+    };
+
+    f32x4 o[MTV];
+#pragma unroll
+    for (int mt = 0; mt < MTV; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+    const int ksig = 4 * (n & 3) + (n >> 2);     // key carried by A-operand row n
+
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+    for (int t = 0; t < n_tiles; ++t) {
+        const int st = t & 1;
+        if (t + 1 < n_tiles) load_tile(t + 1);     // in flight during this tile
+        // partial S^T over this wave's contraction slice
+        f32x4 sp = {0.f, 0.f, 0.f, 0.f};
+        const float* ka = kst + st * KTILE + ksig * KROW + w * QS + g;
+#pragma unroll
+        for (int s = 0; s < KSW; ++s) sp = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[4 * s], qv[s], sp, 0, 0, 0);
+        *(f32x4*)(xs + (w * 64 + lane) * 4) = sp;
+        __syncthreads();
+        f32x4 sc = *(const f32x4*)(xs + lane * 4);
+#pragma unroll
+        for (int v = 1; v < 4; ++v) sc += *(const f32x4*)(xs + (v * 64 + lane) * 4);
+        // online softmax of rows n over keys 16t + 4i + g
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int key = t * kF32Kt + 4 * i + g;
+            if (key >= Tkv || (CAUSAL && key > tok + q_off)) sc[i] = -INFINITY;
+            mx = fmaxf(mx, sc[i]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = fmaxf(m_run, mx * scale_log2);
+        const float alpha = m_run == -INFINITY ? 0.f : fast_exp2(m_run - mnew);
+        const float mu = mnew == -INFINITY ? 0.f : mnew;
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(sc[i], scale_log2, -mu));
+        l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+        m_run = mnew;
+        // O^T += V^T P^T over this wave's value dims
+        const float* va = vst + st * VTILE + g * VROW + w * VS + n;
+#pragma unroll
+        for (int mt = 0; mt < MTV; ++mt) {
+            o[mt] *= alpha;
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                o[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(va[4 * s * VROW + 16 * mt], p[s], o[mt], 0, 0, 0);
+        }
+        if (t + 1 < n_tiles) store_tile(st ^ 1);
+        __syncthreads();
     }
+
+    float l = l_run + __shfl_xor(l_run, 16);      // row sum over the four lane groups
+    l += __shfl_xor(l, 32);
+    if (!row_ok) return;
+    const size_t row = ((size_t)b * Hq + head) * Tq + tok;
+    const float inv = 1.f / l;
+#pragma unroll
+    for (int mt = 0; mt < MTV; ++mt)
+        *(f32x4*)(Out + row * DV + w * VS + 16 * mt + 4 * g) = o[mt] * inv;
+    if (Lse != nullptr && w == 0 && g == 0) Lse[row] = m_run * kLn2 + __logf(l);
 }
 
-// ---------------------------------------------------------------------------
-// Host-side launchers (validated arguments only).
-// ---------------------------------------------------------------------------
 template <int DK, int DV, int NR, int NW, int KT, bool F16>
 static hipError_t launch_16(const PrefillArgs& a) {
     const int R = NW * 32 * NR;
@@ -694,18 +771,19 @@ static hipError_t launch_16(const PrefillArgs& a) {
 
 template <int DK, int DV>
 static hipError_t launch_f32(const PrefillArgs& a) {
-    const int n_blocks = (a.Tq + 15) / 16;
-    const dim3 grid(n_blocks, a.Hq, a.B);
+    const long long rows = (long long)a.Tq * a.G;
+    const int n_blk = (int)((rows + kF32Rows - 1) / kF32Rows);
+    const dim3 grid(n_blk, a.Hkv, a.B);
     const float sl2 = a.scale * kLog2e;
     const int q_off = a.Tkv - a.Tq;
     if (a.causal)
         hipLaunchKernelGGL((prefill_f32_kernel<DK, DV, true>), grid, dim3(256), 0, a.stream, (const float*)a.q,
-                           (const float*)a.k, (const float*)a.v, (float*)a.out, a.lse, a.Hq, a.Hkv, a.Tq, a.Tkv,
-                           q_off, a.G, sl2);
+                           (const float*)a.k, (const float*)a.v, (float*)a.out, a.lse, a.Hq, a.Tq, a.Tkv, q_off, a.G,
+                           n_blk, sl2);
     else
         hipLaunchKernelGGL((prefill_f32_kernel<DK, DV, false>), grid, dim3(256), 0, a.stream, (const float*)a.q,
-                           (const float*)a.k, (const float*)a.v, (float*)a.out, a.lse, a.Hq, a.Hkv, a.Tq, a.Tkv,
-                           q_off, a.G, sl2);
+                           (const float*)a.k, (const float*)a.v, (float*)a.out, a.lse, a.Hq, a.Tq, a.Tkv, q_off, a.G,
+                           n_blk, sl2);
     return hipGetLastError();
 }
 

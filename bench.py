@@ -19,7 +19,7 @@ workload, inputs already resident in HBM:
   * mqa_prefill          the first workload with fp16 inputs and output
   * mqa_prefill          causal MQA in fp32 end to end, B=1, Hq=16, Hkv=1,
                          T=128, d=512 (a latency-sized call on the fp32
-                         VALU kernel; its roofline is the fp32 vector rate)
+                         MFMA kernel; its roofline is the fp32 MFMA rate)
 bf16 in (but the fp16 and fp32 ones), fp32 accumulation, 16-bit out.
 
 W untimed warm-up steps run first, extended (at most 400 steps) until they
@@ -79,7 +79,7 @@ ORDER = (
     ("mqa_prefill_f32_b1_t128", "f32_prefill"),
 )
 
-PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector (256 CUs x 4 SIMD x 64 lanes x 2 flop x 2.4 GHz)
+PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 MFMA
 
 # waves per SIMD of each prefill kernel (the matching measured MFMA ceiling)
 PREFILL_WAVES_PER_SIMD = {512: 1, 128: 2, 192: 2}
@@ -494,7 +494,7 @@ def main():
                 calls[name] = (lambda dq=dq, dk=dk, dv=dv, out=out, ws=ws, sc=sc:
                                mqa.mqa_prefill_ex(dq, dk, dv, causal=True, scale=sc, out=out, workspace=ws))
             if wl.dtype == "f32":
-                work[name] = dict(flops=prefill_flops(**s), bytes=prefill_bytes(**s) * 2, bound="alu", shape=s)
+                work[name] = dict(flops=prefill_flops(**s), bytes=prefill_bytes(**s) * 2, bound="mfma_f32", shape=s)
             else:
                 work[name] = dict(flops=prefill_flops(**s), bytes=prefill_bytes(**s), bound="mfma", shape=s,
                                   waves_per_simd=PREFILL_WAVES_PER_SIMD.get(s["D"], 1))
@@ -633,8 +633,9 @@ def main():
         if w["bound"] == "mfma":
             r["roofline"] = roofline("mfma", tflops, PEAK_BF16_TFLOPS, "TFLOP/s", tr)
             _attainable(r["roofline"], peaks.get(f"mfma_bf16_tflops_{w.get('waves_per_simd', 1)}wave"))
-        elif w["bound"] == "alu":
-            r["roofline"] = roofline("alu", tflops, PEAK_FP32_VALU_TFLOPS, "TFLOP/s", tr)
+        elif w["bound"] == "mfma_f32":
+            # the fp32 MFMA; no probe measures its attainable rate
+            r["roofline"] = roofline("mfma", tflops, PEAK_FP32_MFMA_TFLOPS, "TFLOP/s", tr)
         else:
             r["roofline"] = roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", tr)
             _attainable(r["roofline"], peaks.get("hbm_read_gbs"))
