@@ -179,6 +179,9 @@ int mqa_prefill_ex(const void* q, const void* k, const void* v, void* out, float
     // the bf16 kernels address one (batch, KV head) tile stream with 32-bit
     // byte offsets
     if (bf && ((size_t)T_kv + 31) * ((size_t)d_qk + d_v) * 2 > 0xFFFFFFFFull) return MQA_ERR_UNSUPPORTED;
+    // the fp32 kernel deals the T_q x G rows of a (batch, KV head) in blocks
+    // of 16 over the grid's x dimension
+    if (!bf && ((long long)T_q * G + 15) / 16 > 0x7FFFFFFFLL) return MQA_ERR_UNSUPPORTED;
     const size_t need = mqa_prefill_ex_workspace_size(B, Hq, Hkv, T_q, T_kv, d_qk, d_v, in_dtype);
     if (need > 0) {
         if (!workspace || workspace_bytes < need) return MQA_ERR_WORKSPACE;

@@ -92,7 +92,8 @@ const char* mqa_last_hip_error_name(void);
  *   in_dtype BF16 or F16 -> out_dtype the same or F32, D in {128, 512}, and the group
  *     size G = Hq/Hkv <= 128 (D=512) or G <= 256 (D=128) (any G: a
  *     workgroup takes floor(rows / G) tokens of all G heads);
- *   in_dtype F32 -> out_dtype F32, D a multiple of 64 up to 512, any G.
+ *   in_dtype F32 -> out_dtype F32, D a multiple of 64 up to 512, any G, and
+ *     T * G < 2^35 (the query rows are dealt in blocks of 16).
  * Workspace: 16-bit inputs need `mqa_prefill_workspace_size()` bytes, where the
  * library first writes a transposed V, and at D = 512 also K with padded
  * rows, as one stream of 32-key tiles (B * Hkv * ceil(T/32) * 32 * (D + k)
@@ -129,7 +130,8 @@ int mqa_prefill(const void* q, const void* k, const void* v, void* out, float* l
  *   expanded and decode absorbed; dimensions as in walkerchi.com "Full 路线"
  *   §四 4.2).
  * Supported: everything mqa_prefill supports (d_qk == d_v, as listed there),
- *   plus (d_qk, d_v) = (192, 128) with any G <= 128 (16-bit) or any G (fp32).
+ *   plus (d_qk, d_v) = (192, 128) with any G <= 128 (16-bit) or any G (fp32;
+ *   T_q * G < 2^35 as for mqa_prefill).
  *   T_q == 0 or B == 0 is an empty call; T_kv == 0 with T_q > 0 is rejected.
  * Workspace (16-bit inputs): `mqa_prefill_ex_workspace_size()` bytes =
  *   B * Hkv * ceil(T_kv/32) * 32 * (k + d_v) * 2, k = d_qk + 8 when

@@ -114,6 +114,9 @@ def test_prefill_ex_rejections():
     assert _prefill_ex(DK=512, DV=128) == UNSUPPORTED
     assert _prefill_ex(din=F32, dout=F32, DK=256, DV=128) == UNSUPPORTED
     assert _prefill_ex(Hq=512, Hkv=1) == UNSUPPORTED        # group larger than a workgroup's rows
+    # fp32: T_q x G rows in blocks of 16 must fit the grid (2^35 rows)
+    big = 2 ** 31 - 1
+    assert _prefill_ex(din=F32, dout=F32, Hq=64, Hkv=1, Tq=big, Tkv=big, causal=0, ws=None, wsb=0) == UNSUPPORTED
     assert _prefill_ex(ws=None, wsb=0) == WORKSPACE
     need = lib.mqa_prefill_ex_workspace_size(1, 128, 128, 64, 256, 192, 128, BF16)
     assert _prefill_ex(wsb=need - 1) == WORKSPACE
