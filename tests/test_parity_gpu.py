@@ -77,6 +77,25 @@ def test_prefill_f32_mqa_t128_full(torch, mqa):
     assert _maxerr(host(lse), ref_lse) <= F32_TOL
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,T,D,causal", [
+    (1, 24, 1, 33, 128, True),     # a 16-row block holds part of a token's 24 heads
+    (2, 48, 2, 21, 64, False),     # two KV heads of 24
+    (1, 200, 1, 9, 64, True),      # 200 heads over one KV head: 12.5 blocks per token
+    (1, 5, 1, 70, 256, True),      # blocks straddle tokens (16 = 3 x 5 + 1)
+])
+def test_prefill_f32_group_layouts(torch, mqa, B, Hq, Hkv, T, D, causal):
+    """fp32 prefill rows are dealt in blocks of 16 (token x head-in-group):
+    groups larger than a block and groups that do not divide it."""
+    _say(f"prefill f32 B{B} Hq{Hq} Hkv{Hkv} T{T} D{D} causal={causal}")
+    q, k, v = prefill_inputs(B, Hq, Hkv, T, D, "f32", seed=50 + Hq)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device="cuda")
+    out = mqa.mqa_prefill(dev(torch, q), dev(torch, k), dev(torch, v), causal=causal, lse=lse)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.prefill_ref(q.f32(), k.f32(), v.f32(), 1 / math.sqrt(D), causal)
+    assert _maxerr(host(out), ref) <= F32_TOL
+    assert _maxerr(host(lse), ref_lse) <= F32_TOL
+
+
 PREFILL_SMALL = [
     # B, Hq, Hkv, T, D, causal, out dtype
     (2, 16, 1, 200, 512, True, "bf16"),
