@@ -96,6 +96,5 @@ def measure(read_mib=4096):
         sink = torch.empty(l.mqa_peak_sink_floats(LDS, w), dtype=torch.float32, device=dev)
         iters = 20000
         ms = _time(torch, lambda s: check(l.mqa_peak_lds_read(w, iters, sink.data_ptr(), s), "lds"), 5)
-        res[f"lds_read_bytes_per_clk_cu_{w}wave"] = None
         res[f"lds_read_tbs_{w}wave"] = round(ncu * w * iters * 8 * 1024 / (ms * 1e-3) / 1e12, 2)
     return res

@@ -45,12 +45,14 @@ size_t mqa_peak_sink_floats(int kind, int waves_per_simd);
  * the clock the loop ran at.  clocks: 2 x uint64 on the device. */
 int mqa_peak_mfma_bf16(int waves_per_simd, int iters, float* sink, unsigned long long* clocks, void* stream);
 
-/* Streaming read of `bytes` (a multiple of 16 is read; the rest ignored)
- * with 16-byte non-temporal loads, 8 workgroups of 256 lanes per CU. */
+/* Streaming read of `bytes` (a multiple of 16 is read; the rest ignored):
+ * 4 workgroups of 256 lanes per CU, each reading its own contiguous chunk
+ * with 16-byte non-temporal loads, four 1 KB wave loads in flight. */
 int mqa_peak_hbm_read(const void* src, size_t bytes, float* sink, void* stream);
 
 /* dst <- src for `bytes` (16-byte units; the rest ignored): reads and
- * writes `bytes` each, non-temporal. */
+ * writes `bytes` each, non-temporal, each workgroup over its own contiguous
+ * chunk. */
 int mqa_peak_hbm_copy(const void* src, void* dst, size_t bytes, void* stream);
 
 /* One workgroup of waves_per_cu (1..16) waves per CU; each wave issues
