@@ -162,8 +162,19 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
 #pragma unroll
     for (int j = 0; j < KS - KS_LAT; ++j)
         rope_off[j] = (uint32_t)(kLatB + n * 128 + (((2 * j + h2) ^ layout::mla_rope_swz(n)) * 16));
-    auto kread = [&](const char* st, int ks) {
-        if (ks < KS_LAT) return *(const bf16x8*)(st + lat_off + ks * 32);
+    // A read pattern's per-lane base within the current stage, held in one
+    // VGPR the compiler cannot split again: left to itself it keeps one
+    // loop-invariant offset per read and adds the stage offset to each of
+    // them every tile (two VALU per read); pinned, each read adds only an
+    // immediate offset
+    auto pinned = [&](const char* p) -> const char* {
+        uint32_t off = (uint32_t)(p - smem);
+        asm volatile("" : "+v"(off));
+        return smem + off;
+    };
+    // klat = pinned(stage + lat_off)
+    auto kread = [&](const char* klat, const char* st, int ks) {
+        if (ks < KS_LAT) return *(const bf16x8*)(klat + ks * 32);
         return *(const bf16x8*)(st + rope_off[ks - KS_LAT]);
     };
     // transposing V^T reads: 16-lane group q = lane / 16, lane j = 4s + a in
@@ -173,8 +184,9 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
     const int tj = lane & 15;
     const uint32_t tr_off = (uint32_t)((8 * h2 + 2 * (tj >> 2)) * kLatRowB +
                                        2 * (kDW * w + 16 * ((lane >> 4) & 1) + 4 * (tj & 3)));
-    auto vread = [&](const char* st, int kp, int mt) {
-        const char* p = st + tr_off + kp * 16 * kLatRowB + mt * 64;
+    // vb = pinned(stage + tr_off)
+    auto vread = [&](const char* vb, int kp, int mt) {
+        const char* p = vb + kp * 16 * kLatRowB + mt * 64;
         const s16x4 lo = lds_read_tr16(p);
         const s16x4 hi = lds_read_tr16(p + kLatRowB);
         typedef short s16x8 __attribute__((ext_vector_type(8)));
@@ -194,14 +206,15 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
     // between(ks) runs before step ks's MFMA (work spread over the phase)
     auto scores = [&](const char* st, auto&& between) {
         f32x16 sc = f32x16{};
+        const char* klat = pinned(st + lat_off);
         bf16x8 abuf[PF];
 #pragma unroll
-        for (int j = 0; j < PF; ++j) abuf[j] = kread(st, j);
+        for (int j = 0; j < PF; ++j) abuf[j] = kread(klat, st, j);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             between(ks);
             const bf16x8 a = abuf[ks % PF];
-            if (ks + PF < KS) abuf[ks % PF] = kread(st, ks + PF);
+            if (ks + PF < KS) abuf[ks % PF] = kread(klat, st, ks + PF);
             sc = mfma_32x32x16_t<F16>(a, qb[ks], sc);
         }
         sched_reads_ahead<PF, KS - PF>();
@@ -273,6 +286,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
     // of kp = 1 are read during kp = 0.
     auto pv_tile = [&](int it, auto&& between) {
         const char* st = smem + (it % kNS) * kStageB;
+        const char* vb = pinned(st + tr_off);
         const char* pl = pbuf + (it & 1) * kPB;
         auto pread = [&](int kp, int nt) {
             const int hh = 32 * nt + n;
@@ -283,8 +297,8 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
         bf16x8 va[3];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) pb[0][nt] = pread(0, nt);
-        va[0] = vread(st, 0, 0);
-        va[1] = vread(st, 0, 1);
+        va[0] = vread(vb, 0, 0);
+        va[1] = vread(vb, 0, 1);
         const float* al = alpha_buf + (it & 1) * kHMAX;
         float a4[NT];
         bool need = false;
@@ -302,7 +316,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
         }
 #pragma unroll
         for (int stp = 0; stp < NSTEP; ++stp) {
-            if (stp + 2 < NSTEP) va[(stp + 2) % 3] = vread(st, (stp + 2) / MT, (stp + 2) % MT);
+            if (stp + 2 < NSTEP) va[(stp + 2) % 3] = vread(vb, (stp + 2) / MT, (stp + 2) % MT);
             if (stp == 1) {
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) pb[1][nt] = pread(1, nt);
@@ -354,6 +368,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
             // writes over steps 2..5, the rescale factor at 6
             {
                 const char* st = smem + (it % kNS) * kStageB;
+                const char* vb = pinned(st + tr_off);
                 const char* pl = pbuf + (it & 1) * kPB;
                 auto pread = [&](int kp, int nt) {
                     const int hh = 32 * nt + n;
@@ -364,8 +379,8 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
                 bf16x8 va[3];
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) pb[0][nt] = pread(0, nt);
-                va[0] = vread(st, 0, 0);
-                va[1] = vread(st, 0, 1);
+                va[0] = vread(vb, 0, 0);
+                va[1] = vread(vb, 0, 1);
                 const float* al = alpha_buf + (it & 1) * kHMAX;
                 float a4[NT];
                 bool need = false;
@@ -382,7 +397,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
                 }
 #pragma unroll
                 for (int stp = 0; stp < NSTEP; ++stp) {
-                    if (stp + 2 < NSTEP) va[(stp + 2) % 3] = vread(st, (stp + 2) / MT, (stp + 2) % MT);
+                    if (stp + 2 < NSTEP) va[(stp + 2) % 3] = vread(vb, (stp + 2) / MT, (stp + 2) % MT);
                     if (stp == 1) {
 #pragma unroll
                         for (int nt = 0; nt < NT; ++nt) pb[1][nt] = pread(1, nt);
