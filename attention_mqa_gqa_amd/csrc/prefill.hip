@@ -419,12 +419,15 @@ __global__ __launch_bounds__(NW * 64, (DK == 512 ? 1 : 8 / NW)) void prefill_bf1
         const char* kst = smem + ((it + 1) & 1) * KSTAGE_B;
 #pragma unroll
         for (int nt = 0; nt < NR; ++nt) sn[nt] = f32x16{};
-        // Row sums of P(t): added up next to the exponentials, except at
-        // d_qk = 128, whose phase A is the most exponential-heavy: there
-        // they are taken in phase B from the packed 16-bit probabilities
-        // (the values the MFMAs use), a pair per v_dot2c (≈1 % faster; no
-        // gain at 192, and at 512 the extra live ranges in phase B spill)
+        // Row sums of P(t): at d_qk = 512 the fp32 probabilities are added
+        // up next to the exponentials.  Elsewhere they are taken from the
+        // packed 16-bit probabilities (the values the MFMAs use), a pair per
+        // v_dot2c, half the VALU instructions: at 128 in phase B, whose
+        // phase A is the most exponential-heavy (≈1 % faster), at 192 right
+        // after the packing in phase A (3 % faster; at 512 neither form
+        // gains, and the phase-B one spills)
         constexpr bool SUM_IN_B = DK == 128;
+        constexpr bool SUM_PACKED_A = DK == 192;
         float lsum[NR];
 #pragma unroll
         for (int nt = 0; nt < NR; ++nt) lsum[nt] = 0.f;
@@ -454,7 +457,7 @@ __global__ __launch_bounds__(NW * 64, (DK == 512 ? 1 : 8 / NW)) void prefill_bf1
                         float pr = fast_exp2(fmaf(sc[nt][i], c, -m_run[nt]));
                         asm volatile("" : "+v"(pr));
                         sc[nt][i] = pr;
-                        if constexpr (!SUM_IN_B) lsum[nt] += pr;
+                        if constexpr (!SUM_IN_B && !SUM_PACKED_A) lsum[nt] += pr;
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -463,7 +466,7 @@ __global__ __launch_bounds__(NW * 64, (DK == 512 ? 1 : 8 / NW)) void prefill_bf1
         bf16x8 pb[NR][KSP];
 #pragma unroll
         for (int nt = 0; nt < NR; ++nt) {
-            if constexpr (!SUM_IN_B) {
+            if constexpr (!SUM_IN_B && !SUM_PACKED_A) {
                 l_run[nt] += lsum[nt];
                 asm volatile("" : "+v"(l_run[nt]));
             }
@@ -475,6 +478,11 @@ __global__ __launch_bounds__(NW * 64, (DK == 512 ? 1 : 8 / NW)) void prefill_bf1
                 // keeps the exponentials in phase A: without a use here the
                 // compiler sinks them into phase B, next to the P.V MFMAs
                 asm volatile("" : "+v"(pb[nt][kp]));
+                if constexpr (SUM_PACKED_A) {
+                    const u32x4 wv = __builtin_bit_cast(u32x4, pb[nt][kp]);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) l_run[nt] = add_pair_t<F16>(wv[q], l_run[nt]);
+                }
             }
         }
 
