@@ -621,6 +621,63 @@ def test_mla_step_graph_replay(torch, mqa):
             assert torch.equal(got, want), f"replay {rep}"
 
 
+def test_prefill_and_decode_graph_replay(torch, mqa):
+    """MQA prefill (16-bit with its packing pass, and fp32), GQA prefill and
+    MQA/GQA decode captured once in a HIP graph through the C ABI and
+    replayed three times, with eager work between the replays: every replay
+    equals the eager calls bit for bit (the library records no memset and
+    allocates nothing, so its calls can be captured)."""
+    _say("prefill + decode as a HIP graph")
+    q, k, v = (dev(torch, t) for t in prefill_inputs(1, 16, 1, 300, 512, "bf16", seed=61))
+    qg, kg, vg = (dev(torch, t) for t in prefill_inputs(1, 16, 2, 200, 128, "bf16", seed=62))
+    qf, kf, vf = (dev(torch, t) for t in prefill_inputs(1, 4, 1, 70, 256, "f32", seed=63))
+    dq, dk, dv, sl = decode_inputs(3, 16, 1, 2100, 512, "bf16", seed=64, lengths=[2100, 5, 1000])
+    dq, dk, dv = dev(torch, dq), dev(torch, dk), dev(torch, dv)
+    dsl = torch.from_numpy(sl).cuda()
+    gq, gk, gv, gsl = decode_inputs(2, 32, 4, 1500, 128, "bf16", seed=65, lengths=[1500, 77])
+    gq, gk, gv = dev(torch, gq), dev(torch, gk), dev(torch, gv)
+    gsl = torch.from_numpy(gsl).cuda()
+    outs = [torch.empty((1, 16, 300, 512), dtype=torch.bfloat16, device="cuda"),
+            torch.empty((1, 16, 200, 128), dtype=torch.bfloat16, device="cuda"),
+            torch.empty((1, 4, 70, 256), dtype=torch.float32, device="cuda"),
+            torch.empty((3, 16, 512), dtype=torch.bfloat16, device="cuda"),
+            torch.empty((2, 32, 128), dtype=torch.bfloat16, device="cuda")]
+    lses = [torch.empty((1, 16, 300), dtype=torch.float32, device="cuda"),
+            torch.empty((3, 16), dtype=torch.float32, device="cuda")]
+    ws = [torch.empty(mqa.mqa_prefill_workspace_size(1, 16, 1, 300, 512, mqa.DTYPE_BF16), dtype=torch.uint8, device="cuda"),
+          torch.empty(mqa.mqa_prefill_workspace_size(1, 16, 2, 200, 128, mqa.DTYPE_BF16), dtype=torch.uint8, device="cuda"),
+          torch.empty(mqa.mqa_decode_workspace_size(3, 16, 1, 2100, 512), dtype=torch.uint8, device="cuda"),
+          torch.empty(mqa.mqa_decode_workspace_size(2, 32, 4, 1500, 128), dtype=torch.uint8, device="cuda")]
+
+    def step():
+        mqa.mqa_prefill(q, k, v, causal=True, out=outs[0], lse=lses[0], workspace=ws[0])
+        mqa.mqa_prefill(qg, kg, vg, causal=True, out=outs[1], workspace=ws[1])
+        mqa.mqa_prefill(qf, kf, vf, causal=False, out=outs[2])
+        mqa.mqa_decode(dq, dk, dv, dsl, out=outs[3], lse=lses[1], workspace=ws[2])
+        mqa.mqa_decode(gq, gk, gv, gsl, out=outs[4], workspace=ws[3])
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs + lses]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        for t in outs + lses + ws:
+            t.zero_()                            # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip(outs + lses, ref):
+            assert torch.equal(got, want), f"replay {rep}"
+
+
 # ---------------------------------------------------------------------------
 # sparse (top-k) MLA decode
 # ---------------------------------------------------------------------------
