@@ -1,6 +1,6 @@
 /*
  * mqa_peaks.h -- C ABI of libmqa_peaks.so: probes that measure the ceilings
- * the attention kernels of libmqa_attn.so are judged against, on the device
+ * the attention kernels of libmqa_attn.so are measured against, on the device
  * they run on.  The attention pages give no hardware figures; the rooflines
  * of this library's kernels are (a) the dense bf16 MFMA rate (prefill, and
  * MLA decode, whose 240 flop per byte sits near the ridge) and (b) HBM read
