@@ -55,7 +55,7 @@ constexpr int kMaxSparseChunk = 2048;                            // list entries
 
 // SPARSE = false: sequence b's rows are 0 .. seq_lens[b]-1 (indices unused).
 // SPARSE = true:  its rows are indices[b, 0 .. topk-1] (seq_lens unused).
-template <bool SPARSE, bool F16>
+template <bool SPARSE, bool F16, int NT>
 __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
     const bf16* __restrict__ Qa, const bf16* __restrict__ KV, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ indices, float* __restrict__ part_o, float* __restrict__ part_ml, int H,
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
     constexpr int KS = kDK / 16;         // 36 score steps
     constexpr int KS_LAT = kDC / 16;     // 32 of them over the latent
     constexpr int MT = kDW / 32;         // 4 O^T M-tiles (value dims) per wave
-    constexpr int NT = kHMAX / 32;       // 4 O^T N-tiles (heads)
+    static_assert(NT >= 1 && NT <= kNW, "32-head blocks: 1 .. 4");
     constexpr int PF = 4;                // operand read-ahead
 
     __shared__ __attribute__((aligned(16))) char smem[kLdsB];
@@ -112,6 +112,10 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
     const int n = lane & 31;
     const int head = kHW * w + n;                // head whose scores this lane holds
     const bool head_ok = head < H;
+    // NT blocks of 32 heads (H <= 32 NT): waves 0 .. NT-1 compute the scores
+    // and softmax of one block each; the others only copy and accumulate
+    // O^T, so a small H does not pay for 128 heads' MFMAs
+    const bool scorer = NT == kNW || w < NT;
 
     // q_abs^T operands: lane half h2 holds dims 16ks + 8h2 .. +7 of `head`
     bf16x8 qb[KS];
@@ -344,7 +348,7 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
         // between its MFMAs, and a barrier once tile t+2 has landed.  On the
         // last iteration the scores of the (absent) next tile read a stale
         // stage and are masked away.
-        {
+        if (scorer) {
             f32x16 s0 = scores(smem, nothing);
             sm_max(s0, 0);
 #pragma unroll
@@ -361,9 +365,15 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
             // MFMA chain into short scheduling regions, and the K operand
             // reads would then go out only one or two MFMAs ahead of use
             // (3 % slower)
-            f32x16 sn = scores(smem + ((it + 1) % kNS) * kStageB, [&](int ks) {
-                if (ks % 4 == 0 && ks / 4 < kCopiesPerWave) issue_one(it + 2, ks / 4);
-            });
+            f32x16 sn = f32x16{};
+            if (scorer) {
+                sn = scores(smem + ((it + 1) % kNS) * kStageB, [&](int ks) {
+                    if (ks % 4 == 0 && ks / 4 < kCopiesPerWave) issue_one(it + 2, ks / 4);
+                });
+            } else {
+#pragma unroll
+                for (int i = 0; i < kCopiesPerWave; ++i) issue_one(it + 2, i);
+            }
             // P(t).V(t) as in pv_tile (written out: the register allocator
             // fits this loop without spills only in this form), with the
             // softmax of the next tile: max after step 1, exponentials and P
@@ -407,9 +417,11 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt) mfma_32x32x16_acc_t<F16>(va[stp % 3], pb[stp / MT][nt], o[stp % MT][nt]);
-                    if (stp == 1) sm_max(sn, it + 1);
-                    if (stp >= 2 && stp < 6) sm_exp(sn, it + 1, stp - 2);
-                    if (stp == 6) sm_alpha(it + 1);
+                    if (scorer) {
+                        if (stp == 1) sm_max(sn, it + 1);
+                        if (stp >= 2 && stp < 6) sm_exp(sn, it + 1, stp - 2);
+                        if (stp == 6) sm_alpha(it + 1);
+                    }
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -421,11 +433,13 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
         // flight instead: iteration t computes the scores and softmax of t,
         // barrier, then copies of tile t+2 and P(t).V(t).
         for (int it = 0; it < n_tiles; ++it) {
-            f32x16 sc = scores(smem + (it % kNS) * kStageB, nothing);
-            sm_max(sc, it);
+            if (scorer) {
+                f32x16 sc = scores(smem + (it % kNS) * kStageB, nothing);
+                sm_max(sc, it);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) sm_exp(sc, it, c);
-            sm_alpha(it);
+                for (int c = 0; c < 4; ++c) sm_exp(sc, it, c);
+                sm_alpha(it);
+            }
             // tile it+1 has landed (nothing later was issued yet)
             wait_vmcnt<0>();
             __syncthreads();
@@ -491,13 +505,21 @@ DecodePlan mla_sparse_plan(int B, int topk) {
     return p;
 }
 
-template <bool SPARSE, bool F16>
-static void mla_kernel_launch(const MlaArgs& a) {
+template <bool SPARSE, bool F16, int NT>
+static void mla_kernel_launch_nt(const MlaArgs& a) {
     const dim3 grid(a.plan.n_split, a.B);
-    hipLaunchKernelGGL((mla_decode_kernel<SPARSE, F16>), grid, dim3(kNW * 64), 0, a.stream, (const bf16*)a.q,
+    hipLaunchKernelGGL((mla_decode_kernel<SPARSE, F16, NT>), grid, dim3(kNW * 64), 0, a.stream, (const bf16*)a.q,
                        (const bf16*)a.kv, SPARSE ? (const int32_t*)nullptr : a.seq_lens,
                        SPARSE ? a.indices : (const int32_t*)nullptr, a.part_o, a.part_ml, a.H, a.max_len,
                        SPARSE ? a.topk : 0, a.plan.chunk, a.plan.n_split, a.scale * kLog2e);
+}
+
+// 32-head blocks: 1 for H <= 32, 2 for H <= 64, else 4
+template <bool SPARSE, bool F16>
+static void mla_kernel_launch(const MlaArgs& a) {
+    if (a.H <= 32) mla_kernel_launch_nt<SPARSE, F16, 1>(a);
+    else if (a.H <= 64) mla_kernel_launch_nt<SPARSE, F16, 2>(a);
+    else mla_kernel_launch_nt<SPARSE, F16, 4>(a);
 }
 
 hipError_t mla_launch(const MlaArgs& a) {

@@ -390,6 +390,9 @@ MLA_F16 = [
     (3, 128, 1500, [1500, 31, 777], 0, "f16"),
     (2, 64, 600, [600, 65], 0, "f32"),
     (2, 128, 3000, [3000, 200], 512, "f16"),   # sparse: 512 listed rows (200 for the short sequence)
+    (2, 32, 700, [700, 40], 0, "f16"),          # one block of 32 heads
+    (2, 48, 2000, [2000, 90], 256, "f32"),      # sparse, two head blocks, the second half empty
+    (1, 16, 300, [300], 64, "f16"),             # sparse, one block with 16 heads
 ]
 
 
