@@ -150,7 +150,12 @@ __global__ __launch_bounds__(NW * 64, (DK == 512 ? 1 : 8 / NW)) void prefill_bf1
     static_assert(CV % NW == 0, "V^T tile must split evenly over the waves");
     static_assert((CK % NW) * 64 % NW == 0 && (!KPAD || (PLK == 0 && FK % 4 == 0)), "K tile split");
 
-    __shared__ __attribute__((aligned(16))) char smem[2 * KSTAGE_B + 2 * VSTAGE_B];
+    // 16-bit outputs leave through LDS (rows of 2 DV + 16 bytes, reusing the
+    // stages once the loop is done)
+    constexpr int OROW_B = 2 * DV + 16;
+    constexpr int OUT_LDS_B = OUT_F32 ? 0 : NW * RW * OROW_B;
+    constexpr int SMEM_B = 2 * KSTAGE_B + 2 * VSTAGE_B > OUT_LDS_B ? 2 * KSTAGE_B + 2 * VSTAGE_B : OUT_LDS_B;
+    __shared__ __attribute__((aligned(16))) char smem[SMEM_B];
 
     const int lane = lane_id();
     const int w = wave_id();
@@ -559,32 +564,75 @@ __global__ __launch_bounds__(NW * 64, (DK == 512 ? 1 : 8 / NW)) void prefill_bf1
     wait_vmcnt<0>();    // the copies past the last tile
 
     // ---- epilogue: normalise, store ------------------------------------------
+    // Accumulators 8 half .. 8 half + 7 of tile (mt, nt) are 8 consecutive
+    // value dims of this lane's row.  fp32 rows are stored from registers.
+    // 16-bit rows go through LDS first, so that every store instruction
+    // writes whole rows (1 KB contiguous at d_v = 512, four 256-byte rows at
+    // 128) instead of 16 bytes of each of 32 rows: at d_v = 512 the scattered
+    // stores kept a workgroup 5 us in its epilogue, through LDS about 2.
     mfma_acc_drain();
+    if constexpr (!OUT_F32) __syncthreads();    // every wave is done with the last V^T stage
 #pragma unroll
     for (int nt = 0; nt < NR; ++nt) {
         const float l = sum_over_halves(l_run[nt]);
         const float inv = 1.f / l;
-        if (!row_ok[nt]) continue;
         const size_t row = ((size_t)b * Hq + row_head[nt]) * Tq + row_tok[nt];
+        char* orow = smem + (w * RW + 32 * nt + n) * OROW_B;
+        if (!OUT_F32 || row_ok[nt]) {
 #pragma unroll
-        for (int mt = 0; mt < MT_O; ++mt) {
+            for (int mt = 0; mt < MT_O; ++mt) {
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const f32x16& acc = o[mt][nt];
-                const f32x4 lo = f32x4{acc[8 * half + 0], acc[8 * half + 1], acc[8 * half + 2], acc[8 * half + 3]} * inv;
-                const f32x4 hi = f32x4{acc[8 * half + 4], acc[8 * half + 5], acc[8 * half + 6], acc[8 * half + 7]} * inv;
-                const int d0 = 32 * mt + layout::c32_index(h2, 8 * half);
-                if constexpr (OUT_F32) {
-                    float* dst = (float*)Out + row * DV + d0;
-                    *(f32x4*)dst = lo;
-                    *(f32x4*)(dst + 4) = hi;
-                } else {
-                    bf16* dst = (bf16*)Out + row * DV + d0;
-                    *(bf16x8*)dst = pack8_t<F16>(lo, hi);
+                for (int half = 0; half < 2; ++half) {
+                    const f32x16& acc = o[mt][nt];
+                    const f32x4 lo = f32x4{acc[8 * half + 0], acc[8 * half + 1], acc[8 * half + 2], acc[8 * half + 3]} * inv;
+                    const f32x4 hi = f32x4{acc[8 * half + 4], acc[8 * half + 5], acc[8 * half + 6], acc[8 * half + 7]} * inv;
+                    const int d0 = 32 * mt + layout::c32_index(h2, 8 * half);
+                    if constexpr (OUT_F32) {
+                        float* dst = (float*)Out + row * DV + d0;
+                        *(f32x4*)dst = lo;
+                        *(f32x4*)(dst + 4) = hi;
+                    } else {
+                        *(bf16x8*)(orow + 2 * d0) = pack8_t<F16>(lo, hi);
+                    }
                 }
             }
         }
-        if (Lse != nullptr && h2 == 0) Lse[row] = m_run[nt] * kLn2 + __logf(l);
+        if (Lse != nullptr && h2 == 0 && row_ok[nt]) Lse[row] = m_run[nt] * kLn2 + __logf(l);
+    }
+    if constexpr (!OUT_F32) {
+        __syncthreads();
+        // 16-byte chunk q of row r: a wave instruction covers RPW whole rows,
+        // and a wave's rows are r0, r0 + STEP, ...  All of a wave's LDS reads
+        // go out before its stores (one wait instead of one per row), and
+        // row r = token offset * G + head offset is stepped without divides.
+        constexpr int CPR = DV / 8;                   // chunks per row
+        constexpr int RPW = 64 / CPR;                 // rows per wave instruction
+        constexpr int STEP = NW * RPW;
+        constexpr int ITER = RW * NR / RPW;           // instructions per wave
+        static_assert(64 % CPR == 0 && (RW * NR) % RPW == 0, "row split");
+        const int q = lane % CPR;
+        const int r0 = w * RPW + lane / CPR;
+        u32x4 vals[ITER];
+#pragma unroll
+        for (int k = 0; k < ITER; ++k) vals[k] = *(const u32x4*)(smem + (r0 + k * STEP) * OROW_B + 16 * q);
+        int tok_off = r0 / G, head_off = r0 - tok_off * G;
+        const int dq = STEP / G, dr = STEP - dq * G;
+        // the output pointer moves by one of two strides per step: the head
+        // offset grows by dr (and the token by dq), wrapping past G
+        const long long head_el = (long long)Tq * DV;
+        const long long d_step = dr * head_el + (long long)dq * DV;
+        const long long d_wrap = d_step - G * head_el + DV;
+        bf16* optr = (bf16*)Out + (((size_t)b * Hq + (size_t)hk * G + head_off) * Tq + t0 + tok_off) * DV + 8 * q;
+#pragma unroll
+        for (int k = 0; k < ITER; ++k) {
+            if (r0 + k * STEP < rows_used && t0 + tok_off < Tq) *(u32x4*)optr = vals[k];
+            head_off += dr;
+            tok_off += dq;
+            const bool wrap = head_off >= G;
+            head_off -= wrap ? G : 0;
+            tok_off += wrap ? 1 : 0;
+            optr += wrap ? d_wrap : d_step;
+        }
     }
 }
 
