@@ -34,6 +34,8 @@
 
 namespace mqa {
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 namespace {
 constexpr int kDK = 576;    // key width: latent + RoPE part
 constexpr int kDC = 512;    // latent width (= value width)
@@ -452,23 +454,98 @@ __global__ __launch_bounds__(kNW * 64, 1) void mla_decode_kernel(
     // ---- partials: unnormalised O^T slices, (m, l) per head ---------------------
     mfma_acc_drain();
     const float l_tot = sum_over_halves(l_run);
+    // (m, l) per head, split-major: ((b * n_split + s_idx) * H + head)
     if (head_ok && h2 == 0) {
-        const size_t prow = ((size_t)b * H + head) * n_split + s_idx;
-        part_ml[2 * prow] = m_run;
-        part_ml[2 * prow + 1] = l_tot;
+        const size_t prow = ((size_t)b * n_split + s_idx) * H + head;
+        *(f32x2*)(part_ml + 2 * prow) = f32x2{m_run, l_tot};
     }
+    // O^T partials chunk-major: the 8 value dims 8c .. 8c+7 of head h lie at
+    // ((b * n_split + s_idx) * 64 + c) * H + h (8 floats each), so each store
+    // instruction writes 32 heads' chunk c, 1 KB contiguous (stores of 32
+    // bytes of each of 32 head rows were 2 % slower)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         const int hh = 32 * nt + n;
         if (hh >= H) continue;
-        float* dst = part_o + (((size_t)b * H + hh) * n_split + s_idx) * kDC + kDW * w + 4 * h2;
+        float* dst = part_o + ((size_t)(b * n_split + s_idx) * (kDC / 8) + (kDW / 8) * w) * H * 8 + (size_t)hh * 8 + 4 * h2;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const f32x16& acc = o[mt][nt];
-                *(f32x4*)(dst + 32 * mt + 8 * q) = f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+                *(f32x4*)(dst + (size_t)(4 * mt + q) * H * 8) = f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
             }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Merge of the MLA split partials (the same arithmetic as the decode merge:
+// splits summed in index order, weights 2^(m_s - M), one division), reading
+// the chunk-major layout above: a workgroup takes 32 heads and 4 chunks (32
+// value dims) of one sequence; lane (n, h2) of wave w sums head 32 hg + n,
+// floats 4 h2 .. 4 h2 + 3 of chunk 4 cg + w, so every load instruction
+// reads 1 KB contiguous; the results leave through LDS as row pieces.
+// ---------------------------------------------------------------------------
+template <bool OUT_F32, bool OUT_F16>
+__global__ __launch_bounds__(256) void mla_merge_kernel(const float* __restrict__ part_o,
+                                                        const float* __restrict__ part_ml,
+                                                        const int32_t* __restrict__ seq_lens, void* __restrict__ Out,
+                                                        float* __restrict__ Lse, int H, int max_len, int chunk,
+                                                        int n_split) {
+    constexpr int EB = OUT_F32 ? 4 : 2;              // output element bytes
+    constexpr int TROW_B = 32 * EB + 16;             // LDS row: 32 dims + padding
+    __shared__ __attribute__((aligned(16))) char tile[32 * TROW_B];
+    const int cg = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int n = lane & 31, h2 = lane >> 5;
+    const int h = 32 * hg + n;
+    const bool h_ok = h < H;
+    // seq_lens null: all n_split partials are present (some may be empty:
+    // m = -inf, l = 0, O = 0, which contribute nothing)
+    int ns = n_split;
+    if (seq_lens != nullptr) {
+        const int L = min(max(seq_lens[b], 0), max_len);
+        ns = L > 0 ? (L + chunk - 1) / chunk : 0;
+    }
+    if (!h_ok) ns = 0;
+    const size_t row = (size_t)b * H + (h_ok ? h : 0);
+    // (m, l) of split s: ((b * n_split + s) * H + h), 32 heads' pairs contiguous
+    const float* ml = part_ml + 2 * ((size_t)b * n_split * H + (h_ok ? h : 0));
+    const size_t ml_stride = 2 * (size_t)H;
+    float M = -INFINITY, lsum = 0.f;
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[s * ml_stride]);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const float* src = part_o + ((size_t)b * n_split * (kDC / 8) + 4 * cg + w) * H * 8 + (size_t)h * 8 + 4 * h2;
+    const size_t split_stride = (size_t)(kDC / 8) * H * 8;
+#pragma unroll 4
+    for (int s = 0; s < ns; ++s) {
+        const f32x2 msl = *(const f32x2*)(ml + s * ml_stride);
+        const float f = msl.x == -INFINITY ? 0.f : fast_exp2(msl.x - M);
+        lsum += msl.y * f;
+        acc += *(const f32x4*)(src + s * split_stride) * f;
+    }
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    const f32x4 v = acc * inv;
+    // dims of chunk 4 cg + w within this workgroup's 32: 8 w + 4 h2
+    char* dst = tile + n * TROW_B + (8 * w + 4 * h2) * EB;
+    if constexpr (OUT_F32) {
+        *(f32x4*)dst = v;
+    } else {
+        u32x2 pk;
+        pk.x = pack2_t<OUT_F16>(v.x, v.y);
+        pk.y = pack2_t<OUT_F16>(v.z, v.w);
+        *(u32x2*)dst = pk;
+    }
+    if (Lse != nullptr && cg == 0 && w == 0 && h2 == 0 && h_ok) Lse[row] = lsum > 0.f ? M * kLn2 + __logf(lsum) : -INFINITY;
+    __syncthreads();
+    // 32 row pieces of 32 * EB bytes, 16 bytes per thread
+    constexpr int CPR = 32 * EB / 16;                // 16-byte chunks per row piece
+    if ((int)threadIdx.x < 32 * CPR) {
+        const int r = (int)threadIdx.x / CPR, q = (int)threadIdx.x % CPR;
+        if (32 * hg + r < H) {
+            char* out = (char*)Out + (((size_t)b * H + 32 * hg + r) * kDC + 32 * cg) * EB + 16 * q;
+            *(u32x4*)out = *(const u32x4*)(tile + r * TROW_B + 16 * q);
+        }
     }
 }
 
@@ -532,8 +609,16 @@ hipError_t mla_launch(const MlaArgs& a) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // sparse: every split of every sequence wrote a partial (seq_lens = null)
-    return merge_launch(a.part_o, a.part_ml, sparse ? nullptr : a.seq_lens, a.out, a.lse, a.B, a.H, a.max_len, kDC,
-                        a.plan.chunk, a.plan.n_split, a.out_f32, a.f16, a.stream);
+    const dim3 grid(kDC / 32, (a.H + 31) / 32, a.B);
+    const int32_t* sl = sparse ? nullptr : a.seq_lens;
+#define MQA_MLA_MERGE(F32, F16)                                                                          \
+    hipLaunchKernelGGL((mla_merge_kernel<F32, F16>), grid, dim3(256), 0, a.stream, a.part_o, a.part_ml, sl, \
+                       a.out, a.lse, a.H, a.max_len, a.plan.chunk, a.plan.n_split)
+    if (a.out_f32) MQA_MLA_MERGE(true, false);
+    else if (a.f16) MQA_MLA_MERGE(false, true);
+    else MQA_MLA_MERGE(false, false);
+#undef MQA_MLA_MERGE
+    return hipGetLastError();
 }
 
 }  // namespace mqa
