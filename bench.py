@@ -296,10 +296,10 @@ CALL_KERNELS = {
     "mqa_decode_bf16_b64_l8192": ("decode_split_kernel<512", "lse_merge_kernel<512"),
     "gqa_prefill_bf16_b1_t8192": ("kv_pack_kernel<128", "prefill_bf16_kernel<128"),
     "gqa_decode_bf16_b128_l1024to16384": ("decode_split_kernel<128", "lse_merge_kernel<128"),
-    "mla_decode_bf16_b32_l32768": ("mla_decode_kernel<false", "lse_merge_kernel<512"),
+    "mla_decode_bf16_b32_l32768": ("mla_decode_kernel<false", "mla_merge_kernel"),
     "mla_prefill_bf16_b1_h128_t8192": ("kv_pack_kernel<192", "prefill_bf16_kernel<192"),
     "mqa_chunk_prefill_bf16_b2_q1024_kv8192": ("kv_pack_kernel<512", "prefill_bf16_kernel<512"),
-    "mla_sparse_decode_bf16_b32_l32768_k2048": ("mla_decode_kernel<true", "lse_merge_kernel<512"),
+    "mla_sparse_decode_bf16_b32_l32768_k2048": ("mla_decode_kernel<true", "mla_merge_kernel"),
     "mla_step_proj_bf16_b32_h128": ("mla_absorb_kernel", "mla_cache_append_kernel", "mla_out_proj_kernel"),
     "mqa_prefill_f16_b2_t4096": ("kv_pack_kernel<512", "prefill_bf16_kernel<512"),
     "mqa_prefill_f32_b1_t128": ("prefill_f32_kernel<512",),
@@ -353,6 +353,8 @@ def kernel_trace_summary(d):
                 continue
             kname = next(k for k, a in zip(names, asg) if a == (n, i)).split("(")[0].replace("void ", "").replace("mqa::", "")
             lines.append(f"{n:40s} {kname[:84]:84s} {len(v):6d} {np.mean(v):9.1f} {np.min(v):9.1f} {np.max(v):9.1f}")
+    stray = sum(1 for k, a in zip(names, asg) if a is None and "mqa::" in k)
+    lines.append(f"library dispatches outside the step sequence (set-up calls): {stray}")
     return "\n".join(lines), per
 
 

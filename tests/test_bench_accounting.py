@@ -69,3 +69,23 @@ def test_dispatch_assignment_keeps_shared_kernel_names_apart():
     k = ["mqa::kv_pack_kernel<512, 512, 32>", "mqa::prefill_bf16_kernel<512, 512, 1, 4, 32, true, false, false>"]
     got = bench.assign_dispatches(k * 4, names)
     assert got == [(names[0], 0), (names[0], 1), (names[1], 0), (names[1], 1)] * 2
+
+
+def test_dispatch_assignment_covers_a_whole_step():
+    # one dispatch per kernel slot of every workload, in step order, twice:
+    # every dispatch is assigned (a stale pattern would leave the walk
+    # waiting and drop whole steps)
+    seq = []
+    for n, _ in bench.ORDER:
+        seq += [f"void mqa::{pat}_x>(...)" for pat in bench.CALL_KERNELS[n]]
+    got = bench.assign_dispatches(seq + seq)
+    assert all(a is not None for a in got)
+    assert sum(1 for a in got if a == (bench.ORDER[0][0], 0)) == 2
+
+
+def test_mla_workloads_name_the_mla_merge():
+    # the MLA decodes merge their partials with their own kernel
+    for n in ("mla_decode_bf16_b32_l32768", "mla_sparse_decode_bf16_b32_l32768_k2048"):
+        assert bench.CALL_KERNELS[n][1] == "mla_merge_kernel"
+    src = open(os.path.join(ROOT, "attention_mqa_gqa_amd", "csrc", "mla_decode.hip")).read()
+    assert "mla_merge_kernel<" in src and "merge_launch(" not in src
