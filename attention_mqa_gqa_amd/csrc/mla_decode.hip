@@ -512,13 +512,34 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(const float* __restrict_
     // (m, l) of split s: ((b * n_split + s) * H + h), 32 heads' pairs contiguous
     const float* ml = part_ml + 2 * ((size_t)b * n_split * H + (h_ok ? h : 0));
     const size_t ml_stride = 2 * (size_t)H;
-    float M = -INFINITY, lsum = 0.f;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[s * ml_stride]);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     const float* src = part_o + ((size_t)b * n_split * (kDC / 8) + 4 * cg + w) * H * 8 + (size_t)h * 8 + 4 * h2;
     const size_t split_stride = (size_t)(kDC / 8) * H * 8;
-#pragma unroll 4
-    for (int s = 0; s < ns; ++s) {
+    // the first NC splits' (m, l) and partials are loaded once, all at once
+    // (splits past this sequence's count are loaded while inside the
+    // workspace and then ignored, never multiplied)
+    constexpr int NC = 8;
+    f32x2 mlc[NC];
+    f32x4 pc[NC];
+#pragma unroll
+    for (int s = 0; s < NC; ++s) {
+        const bool in = s < ns;
+        mlc[s] = in ? *(const f32x2*)(ml + s * ml_stride) : f32x2{-INFINITY, 0.f};
+        pc[s] = (s < n_split && h_ok) ? *(const f32x4*)(src + s * split_stride) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float M = -INFINITY, lsum = 0.f;
+#pragma unroll
+    for (int s = 0; s < NC; ++s) M = fmaxf(M, mlc[s].x);
+    for (int s = NC; s < ns; ++s) M = fmaxf(M, ml[s * ml_stride]);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NC; ++s) {
+        if (s < ns) {
+            const float f = mlc[s].x == -INFINITY ? 0.f : fast_exp2(mlc[s].x - M);
+            lsum += mlc[s].y * f;
+            acc += pc[s] * f;
+        }
+    }
+    for (int s = NC; s < ns; ++s) {
         const f32x2 msl = *(const f32x2*)(ml + s * ml_stride);
         const float f = msl.x == -INFINITY ? 0.f : fast_exp2(msl.x - M);
         lsum += msl.y * f;
