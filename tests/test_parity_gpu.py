@@ -385,6 +385,27 @@ def test_mla_small(torch, mqa, B, H, L, lengths, odt):
     assert _maxerr(host(lse), ref_lse) <= BF16_TOL
 
 
+@pytest.mark.parametrize("odt", ["bf16", "f32"])
+def test_mla_merge_many_splits_ignores_unwritten_partials(torch, mqa, odt):
+    """12 splits per sequence (more than the merge keeps in registers), a
+    short second sequence whose later splits write no partial, 48 heads (the
+    second 32-head group half empty), and a workspace filled with NaN first:
+    only the partials this call wrote may reach the output."""
+    _say(f"mla merge: 12 splits, lengths [6000, 700], H48, NaN workspace, out={odt}")
+    B, H, L = 2, 48, 6000
+    q, kv, sl = mla_inputs(B, H, L, 576, "bf16", seed=13, lengths=[6000, 700])
+    ws = torch.full((mqa.mla_decode_workspace_size(B, H, L),), 0xFF, dtype=torch.uint8, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    out_dtype = torch.float32 if odt == "f32" else torch.bfloat16
+    out = mqa.mla_decode_absorbed(dev(torch, q), dev(torch, kv), torch.from_numpy(sl).cuda(), lse=lse,
+                                  out_dtype=out_dtype, workspace=ws)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.mla_absorbed_ref(q.f32(), kv.f32(), sl, 1 / math.sqrt(192))
+    assert np.all(np.isfinite(host(out)))
+    assert _maxerr(host(out), ref) <= BF16_TOL
+    assert _maxerr(host(lse), ref_lse) <= BF16_TOL
+
+
 MLA_F16 = [
     # B, H, L_max, lengths, topk (0: dense), out dtype
     (3, 128, 1500, [1500, 31, 777], 0, "f16"),
